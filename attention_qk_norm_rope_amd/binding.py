@@ -1,0 +1,214 @@
+"""Thin ctypes binding of libdit_attn.so (argument marshalling only).
+
+Every step of the path runs in the library's HIP kernels; this module only
+checks tensor metadata, passes ``data_ptr()`` values, sizes and the current
+torch stream, and turns a non-zero status into ``DitAttnError``.  There is no
+fallback: if the library is missing, the first call raises.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already mapped (both carry the soname libamdhip64.so.7),
+and torch's stream handles are valid inside it.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdit_attn.so")
+
+DIT_BF16 = 0
+DIT_FP32 = 1
+
+_lib = None
+
+
+class DitAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m attention_qk_norm_rope_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.qk_norm_rope.argtypes = [p, p, p, p, p, p, f32, i32, i32, i32, i32, p]
+    lib.attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_fwd_kv_strided.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
+    for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_merge"):
+        getattr(lib, name).restype = i32
+    lib.dit_attn_status_string.argtypes = [i32]
+    lib.dit_attn_status_string.restype = ctypes.c_char_p
+    lib.dit_attn_version.argtypes = []
+    lib.dit_attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def library_path() -> str:
+    _load()
+    return LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return _load().dit_attn_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return _load().dit_attn_version().decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DitAttnError(fn, status, status_string(status))
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return DIT_BF16
+    if t.dtype == torch.float32:
+        return DIT_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def qk_norm_rope(q, k, w_q, w_k, cos, sin, eps: float):
+    """In-place per-head RMSNorm + interleaved RoPE of q and/or k (bf16 BNSD).
+
+    Either q or k may be None.  w_q/w_k: fp32 [D]; cos, sin: fp32 [S, D].
+    """
+    ref = q if q is not None else k
+    if ref is None:
+        raise ValueError("q and k are both None")
+    dev = ref.device
+    B, H, S, D = ref.shape
+    for t, name in ((q, "q"), (k, "k")):
+        if t is not None:
+            _need(t, name, torch.bfloat16, dev)
+            if tuple(t.shape) != (B, H, S, D) or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous [{B},{H},{S},{D}]")
+    for t, name, use in ((w_q, "w_q", q is not None), (w_k, "w_k", k is not None)):
+        if use:
+            _need(t, name, torch.float32, dev)
+            if tuple(t.shape) != (D,) or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous [{D}]")
+    for t, name in ((cos, "cos"), (sin, "sin")):
+        _need(t, name, torch.float32, dev)
+        if tuple(t.shape) != (S, D) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [{S},{D}]")
+    st = _load().qk_norm_rope(_ptr(q), _ptr(k), _ptr(w_q if q is not None else None),
+                              _ptr(w_k if k is not None else None), _ptr(cos), _ptr(sin),
+                              float(eps), B, H, S, D, _stream())
+    _check("qk_norm_rope", st)
+    return q, k
+
+
+def _kv_bh_stride(t, B, H, S, D) -> int | None:
+    """Stride between (b,h) slabs if t is [B,H,S,D] with rows of D contiguous
+    elements and the slabs evenly spaced (contiguous, or a window along S)."""
+    if tuple(t.shape) != (B, H, S, D):
+        return None
+    s0, s1, s2, s3 = t.stride()
+    if s3 != 1 or s2 != D:
+        return None
+    if H > 1 and B > 1 and s0 != H * s1:
+        return None
+    if H == 1:
+        s1 = s0 if B > 1 else S * D
+    return s1
+
+
+def attn_fwd(q, k, v, out=None, lse=None, scale: float | None = None, causal: bool = False,
+             out_dtype=torch.bfloat16, return_lse: bool = True):
+    """softmax(scale * q k^T) v with per-row LSE (natural log), BNSD.
+
+    q: bf16 [B,H,Sq,D] contiguous.  k, v: bf16 [B,H,Skv,D], contiguous or
+    windows along S of longer per-head buffers (same strides for k and v).
+    Returns (out, lse); lse is None when return_lse is False and no lse given.
+    """
+    _need(q, "q", torch.bfloat16, q.device)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, dev)
+    _need(v, "v", torch.bfloat16, dev)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D BNSD")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    sk = _kv_bh_stride(k, B, H, Skv, D)
+    sv = _kv_bh_stride(v, B, H, Skv, D)
+    if sk is None or sv is None or sk != sv:
+        raise ValueError("k and v must be [B,H,Skv,D] with contiguous rows and the same (b,h) stride")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=dev)
+    else:
+        if tuple(out.shape) != (B, H, Sq, D) or not out.is_contiguous():
+            raise ValueError("out must be contiguous [B,H,Sq,D]")
+        if out.device != dev:
+            raise ValueError("out is on another device")
+    code = _dtype_code(out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+        if tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
+            raise ValueError("lse must be contiguous fp32 [B,H,Sq]")
+    lib = _load()
+    if k.is_contiguous() and v.is_contiguous():
+        st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, Skv, D,
+                          float(scale), 1 if causal else 0, code, _stream())
+        _check("attn_fwd", st)
+    else:
+        st = lib.attn_fwd_kv_strided(_ptr(q), _ptr(k), _ptr(v), int(sk), _ptr(out), _ptr(lse), B, H,
+                                     Sq, Skv, D, float(scale), 1 if causal else 0, code, _stream())
+        _check("attn_fwd_kv_strided", st)
+    return out, lse
+
+
+def attn_merge(out_a, lse_a, out_b, lse_b):
+    """In-place merge of (out_b, lse_b) into (out_a, lse_a).  Returns them."""
+    dev = out_a.device
+    if out_a.dim() != 4:
+        raise ValueError("out_a must be [B,H,Sq,D]")
+    B, H, Sq, D = out_a.shape
+    for t, name in ((out_a, "out_a"), (out_b, "out_b")):
+        if tuple(t.shape) != (B, H, Sq, D) or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be contiguous [{B},{H},{Sq},{D}] on {dev}")
+    for t, name in ((lse_a, "lse_a"), (lse_b, "lse_b")):
+        _need(t, name, torch.float32, dev)
+        if tuple(t.shape) != (B, H, Sq) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous fp32 [{B},{H},{Sq}]")
+    st = _load().attn_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), B, H, Sq, D,
+                            _dtype_code(out_a), _dtype_code(out_b), _stream())
+    _check("attn_merge", st)
+    return out_a, lse_a

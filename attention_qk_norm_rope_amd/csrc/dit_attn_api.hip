@@ -1,0 +1,131 @@
+// C ABI of libdit_attn.so: argument validation, then one launch on the
+// caller's stream.  Declarations and the meaning of every argument are in
+// include/dit_attn.h.  Nothing here allocates, synchronises or falls back:
+// a call either enqueues its kernel or returns a status before launching.
+#include "../../include/dit_attn.h"
+#include "internal.h"
+
+#include <math.h>
+#include <stdint.h>
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+    const uintptr_t lo = (uintptr_t)p;
+    return Range{lo, lo + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+constexpr int64_t kMaxElems = (int64_t)1 << 46;  // keeps every byte count far from overflow
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k, const float* cos_t,
+                 const float* sin_t, float eps, int B, int H, int S, int D, hipStream_t stream) {
+    if ((!q && !k) || !cos_t || !sin_t) return DIT_ERR_NULL;
+    if ((q && !w_q) || (k && !w_k)) return DIT_ERR_NULL;
+    if (B < 1 || H < 1 || S < 1 || D < 1) return DIT_ERR_SHAPE;
+    if (!(eps >= 0.f) || !isfinite(eps)) return DIT_ERR_SHAPE;
+    if (D != 64 && D != 128) return DIT_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    const int64_t elems = BH * S * D;
+    if (BH > 0x7FFFFFFF || elems > kMaxElems) return DIT_ERR_SHAPE;
+    if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)) || !aligned(cos_t, 16) || !aligned(sin_t, 16) ||
+        (w_q && q && !aligned(w_q, 16)) || (w_k && k && !aligned(w_k, 16)))
+        return DIT_ERR_ALIGN;
+    const Range rq = range_of(q, q ? elems * 2 : 0), rk = range_of(k, k ? elems * 2 : 0);
+    const Range rc = range_of(cos_t, (int64_t)S * D * 4), rs = range_of(sin_t, (int64_t)S * D * 4);
+    const Range rwq = range_of(w_q, q ? (int64_t)D * 4 : 0), rwk = range_of(w_k, k ? (int64_t)D * 4 : 0);
+    if (q && k && overlap(rq, rk)) return DIT_ERR_ALIAS;
+    for (Range out : {rq, rk}) {
+        if (out.lo == out.hi) continue;
+        for (Range in : {rc, rs, rwq, rwk})
+            if (in.lo != in.hi && overlap(out, in)) return DIT_ERR_ALIAS;
+    }
+    (void)hipGetLastError();  // report only this launch's error
+    return hip_status(dit::launch_qk_norm_rope(q, k, q ? w_q : nullptr, k ? w_k : nullptr, cos_t, sin_t,
+                                               eps, (int)BH, S, D, stream));
+}
+
+int attn_fwd_kv_strided(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out,
+                        float* lse, int B, int H, int Sq, int Skv, int D, float scale, int causal,
+                        int out_dtype, hipStream_t stream) {
+    if (!q || !k || !v || !out) return DIT_ERR_NULL;
+    if (B < 1 || H < 1 || Sq < 1 || Skv < 1 || D < 1) return DIT_ERR_SHAPE;
+    if (!isfinite(scale)) return DIT_ERR_SHAPE;
+    if (D != 64 && D != 128) return DIT_ERR_UNSUPPORTED;
+    if (out_dtype != DIT_BF16 && out_dtype != DIT_FP32) return DIT_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    const int64_t q_elems = BH * Sq * D;
+    if (BH > 0x7FFFFFFF || q_elems > kMaxElems) return DIT_ERR_SHAPE;
+    if (kv_bh_stride < (int64_t)Skv * D) return DIT_ERR_SHAPE;
+    if (kv_bh_stride > kMaxElems || (BH - 1) * kv_bh_stride > kMaxElems) return DIT_ERR_SHAPE;
+    if (kv_bh_stride % 8 != 0) return DIT_ERR_ALIGN;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+        return DIT_ERR_ALIGN;
+    const int64_t kv_elems = (BH - 1) * kv_bh_stride + (int64_t)Skv * D;
+    const Range rq = range_of(q, q_elems * 2), rk = range_of(k, kv_elems * 2), rv = range_of(v, kv_elems * 2);
+    const Range ro = range_of(out, q_elems * (out_dtype == DIT_FP32 ? 4 : 2));
+    const Range rl = range_of(lse, lse ? BH * Sq * 4 : 0);
+    if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return DIT_ERR_ALIAS;
+    if (lse && (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ro))) return DIT_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, (int)BH, Sq, Skv, D, scale,
+                                           causal != 0, out_dtype == DIT_FP32, stream));
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Sq,
+             int Skv, int D, float scale, int causal, int out_dtype, hipStream_t stream) {
+    if (Skv < 1 || D < 1) return !q || !k || !v || !out ? DIT_ERR_NULL : DIT_ERR_SHAPE;
+    return attn_fwd_kv_strided(q, k, v, (int64_t)Skv * D, out, lse, B, H, Sq, Skv, D, scale, causal,
+                               out_dtype, stream);
+}
+
+int attn_merge(void* out_a, float* lse_a, const void* out_b, const float* lse_b, int B, int H, int Sq,
+               int D, int a_dtype, int b_dtype, hipStream_t stream) {
+    if (!out_a || !lse_a || !out_b || !lse_b) return DIT_ERR_NULL;
+    if (B < 1 || H < 1 || Sq < 1 || D < 1) return DIT_ERR_SHAPE;
+    if (D != 64 && D != 128) return DIT_ERR_UNSUPPORTED;
+    if ((a_dtype != DIT_BF16 && a_dtype != DIT_FP32) || (b_dtype != DIT_BF16 && b_dtype != DIT_FP32))
+        return DIT_ERR_UNSUPPORTED;
+    const int64_t rows = (int64_t)B * H * Sq;
+    if (rows * D > kMaxElems) return DIT_ERR_SHAPE;
+    if (!aligned(out_a, 16) || !aligned(out_b, 16) || !aligned(lse_a, 4) || !aligned(lse_b, 4))
+        return DIT_ERR_ALIGN;
+    const Range ra = range_of(out_a, rows * D * (a_dtype == DIT_FP32 ? 4 : 2));
+    const Range rb = range_of(out_b, rows * D * (b_dtype == DIT_FP32 ? 4 : 2));
+    const Range rla = range_of(lse_a, rows * 4), rlb = range_of(lse_b, rows * 4);
+    if (overlap(ra, rla) || overlap(rb, ra) || overlap(rb, rla) || overlap(rlb, ra) || overlap(rlb, rla))
+        return DIT_ERR_ALIAS;
+    (void)hipGetLastError();
+    return hip_status(dit::launch_attn_merge(out_a, lse_a, out_b, lse_b, rows, D, a_dtype == DIT_FP32,
+                                             b_dtype == DIT_FP32, stream));
+}
+
+const char* dit_attn_status_string(int status) {
+    switch (status) {
+        case DIT_OK: return "ok";
+        case DIT_ERR_NULL: return "a required pointer is NULL";
+        case DIT_ERR_SHAPE: return "invalid size, stride or scalar argument";
+        case DIT_ERR_UNSUPPORTED: return "unsupported head dimension or dtype code";
+        case DIT_ERR_ALIGN: return "pointer or stride breaks the alignment rule";
+        case DIT_ERR_ALIAS: return "an output overlaps an input it must not overlap";
+        case DIT_ERR_HIP: return "the HIP runtime reported a launch error";
+        default: return "unknown status";
+    }
+}
+
+const char* dit_attn_version(void) { return "dit_attn 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,24 @@
+// Internal launch interface between the C-ABI layer (dit_attn_api.hip) and the
+// gfx950 kernels.  Arguments are already validated when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+// Attention: q [BH,Sq,D] bf16; k/v rows at k + bh*kv_bh_stride + j*D.
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
+                           void* out, float* lse, int BH, int Sq, int Skv, int D, float scale,
+                           bool causal, bool out_f32, hipStream_t stream);
+
+// RMSNorm + interleaved rotary, in place; q or k may be null.
+hipError_t launch_qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k,
+                               const float* cos_t, const float* sin_t, float eps, int BH, int S,
+                               int D, hipStream_t stream);
+
+// out/LSE merge in place into (out_a, lse_a).
+hipError_t launch_attn_merge(void* out_a, float* lse_a, const void* out_b, const float* lse_b,
+                             int64_t rows, int D, bool a_f32, bool b_f32, hipStream_t stream);
+
+}  // namespace dit

@@ -9,16 +9,21 @@ The workloads stand in for the models the pages run (Qwen-Image, Cosmos
 Predict2.5, Wan2.2), whose weights and data are not available: N(0,1)
 tensors in the models' attention shapes.
 
-Recipe (every config): ``numpy.random.default_rng(seed)`` (PCG64); draw q,
-then k, then v with ``standard_normal(dtype=float32)`` in C order, one
-[S, D] slab per (b, h) in (b, h) order; then w_q and w_k ~ U(0.5, 1.5) as
-float32 [D].  q, k, v are rounded to bf16 (round to nearest even) once.  The
-seed is the config number; config 5 reuses config 4's tensors.
+Recipe (every config): ``numpy.random.SeedSequence(seed).spawn(3*B*H + 1)``
+gives one PCG64 stream per [S, D] slab -- stream t*B*H + b*H + h fills slab
+(b, h) of tensor t (q = 0, k = 1, v = 2) with ``standard_normal(dtype=float32)``
+in C order -- and the last stream draws w_q then w_k ~ U(0.5, 1.5) as float32
+[D].  q, k, v are rounded to bf16 (round to nearest even) once.  Independent
+streams let the slabs be filled in parallel with a result that does not
+depend on the thread count.  The seed is the config number; config 5 reuses
+config 4's tensors.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -28,11 +33,15 @@ import numpy as np
 
 def to_bf16_bits(x) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
-    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = f.view(np.uint32)
-    rounded = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16))
-    bits = rounded.astype(np.uint16)
+    f = np.array(x, dtype=np.float32, copy=True, order="C")
     nan = np.isnan(f)
+    u = f.view(np.uint32)
+    lsb = u >> np.uint32(16)
+    lsb &= np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
+    bits = u.astype(np.uint16)
     if nan.any():
         bits[nan] = np.uint16(0x7FC0)
     return bits
@@ -99,12 +108,12 @@ CONFIGS = {
 # --------------------------------------------------------------------------
 # Random tensors
 
-def _normal_bits(rng: np.random.Generator, B: int, H: int, S: int, D: int) -> np.ndarray:
-    out = np.empty((B, H, S, D), dtype=np.uint16)
-    for b in range(B):
-        for h in range(H):
-            out[b, h] = to_bf16_bits(rng.standard_normal((S, D), dtype=np.float32))
-    return out
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def make_inputs(cfg: Config) -> dict:
@@ -112,12 +121,22 @@ def make_inputs(cfg: Config) -> dict:
 
     For config 5 the returned q is config 4's q restricted to rows [0, Sq).
     """
-    rng = np.random.default_rng(cfg.seed)
-    q = _normal_bits(rng, cfg.B, cfg.H, cfg.S, cfg.D)
-    k = _normal_bits(rng, cfg.B, cfg.H, cfg.S, cfg.D)
-    v = _normal_bits(rng, cfg.B, cfg.H, cfg.S, cfg.D)
-    w_q = rng.uniform(0.5, 1.5, size=cfg.D).astype(np.float32)
-    w_k = rng.uniform(0.5, 1.5, size=cfg.D).astype(np.float32)
+    B, H, S, D = cfg.B, cfg.H, cfg.S, cfg.D
+    streams = np.random.SeedSequence(cfg.seed).spawn(3 * B * H + 1)
+    tensors = [np.empty((B, H, S, D), dtype=np.uint16) for _ in range(3)]
+
+    def fill(job):
+        t, bh = job
+        rng = np.random.default_rng(streams[t * B * H + bh])
+        tensors[t][bh // H, bh % H] = to_bf16_bits(rng.standard_normal((S, D), dtype=np.float32))
+
+    jobs = [(t, bh) for t in range(3) for bh in range(B * H)]
+    with concurrent.futures.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, jobs))
+    wrng = np.random.default_rng(streams[-1])
+    w_q = wrng.uniform(0.5, 1.5, size=D).astype(np.float32)
+    w_k = wrng.uniform(0.5, 1.5, size=D).astype(np.float32)
+    q, k, v = tensors
     if cfg.sq is not None:
         q = np.ascontiguousarray(q[:, :, : cfg.sq])
     return {"q": q, "k": k, "v": v, "w_q": w_q, "w_k": w_k}

@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of the DiT attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan|qwen|cosmos|sp]
+                    [--no-cpu-baseline]
+
+One step is one pass of the whole path over one batch of synthetic input.
+Default workload (Wan2.2 shape, B1 H40 S75600 D128, bf16 ~ N(0,1)), laid out
+as the Ring Attention Overlap of the Wan2.2 NPU page on one GPU:
+  1. restore q, k from pristine device copies (the prologue works in place),
+  2. qk_norm_rope(q, k): per-head RMSNorm (eps 1e-5) + 3D interleaved RoPE,
+  3. attn_fwd over the local quarter of the keys      -> fp32 out_a, lse_a,
+  4. attn_fwd over the remaining three quarters (a window of the same K/V)
+                                                      -> fp32 out_b, lse_b,
+  5. attn_merge(out_a, lse_a, out_b, lse_b).
+Steps 3+4 cover every key once, so the attention work is exactly that of
+full attention: 4*B*H*Sq*Skv*D FLOP per step.
+
+`value` is that attention FLOP count divided by the whole step's time
+(TFLOP/s).  Kernel durations come from HIP events recorded on the stream the
+kernels are launched on (torch's current stream).  The CPU baseline times the
+fp64 oracle on a bounded sample of query rows on the host cores.
+
+Other workloads (--workload) are per-config measurements:
+  qwen / cosmos: restore, prologue, attn_fwd over all keys;
+  sp: 4 x attn_fwd over KV chunks of 18900 keys + 3 fp32 merges (Sq 18900).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s and % of bf16 MFMA peak at 1 MI355X; oracle-match"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan", choices=["wan", "qwen", "cosmos", "sp"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def traffic_entry(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    e = data.get(kernel, {}).get(workload)
+    if not e:
+        return None
+    src = os.path.join(ROOT, "attention_qk_norm_rope_amd", "csrc", e["source"])
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return e["bytes_per_launch"] if digest == e["sha256"] else None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the path would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from attention_qk_norm_rope_amd import attn_fwd, attn_merge, inputs, qk_norm_rope
+    from attention_qk_norm_rope_amd import binding
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding._load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wl = args.workload
+    cfg = {"wan": inputs.CONFIGS[4], "qwen": inputs.CONFIGS[2], "cosmos": inputs.CONFIGS[3],
+           "sp": inputs.CONFIGS[5]}[wl]
+    log(f"[bench] generating inputs for {cfg.name}")
+    t0 = time.time()
+    x = inputs.make_inputs(cfg)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+    B, H, D, S = cfg.B, cfg.H, cfg.D, cfg.S
+    Sq, Skv = cfg.Sq, cfg.Skv
+    scale = cfg.scale
+
+    q0 = to_dev(x["q"])
+    k0 = to_dev(x["k"])
+    v = to_dev(x["v"])
+    q = torch.empty_like(q0)
+    k = torch.empty_like(k0)
+    events = []
+    kernels = {}
+
+    if wl in ("wan", "qwen", "cosmos"):
+        cos, sin = inputs.config_rope_tables(cfg)
+        cos_d = torch.from_numpy(cos).to(dev)
+        sin_d = torch.from_numpy(sin).to(dev)
+        w_q = torch.from_numpy(x["w_q"]).to(dev)
+        w_k = torch.from_numpy(x["w_k"]).to(dev)
+
+    if wl == "wan":
+        c = S // 4
+        out_a = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+        out_b = torch.empty_like(out_a)
+        lse_a = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+        lse_b = torch.empty_like(lse_a)
+        names = ["qk_norm_rope", "attn_fwd", "attn_fwd", "attn_merge"]
+
+        def step(ev):
+            q.copy_(q0)
+            k.copy_(k0)
+            ev[0].record()
+            qk_norm_rope(q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
+            ev[1].record()
+            attn_fwd(q, k[:, :, :c], v[:, :, :c], out=out_a, lse=lse_a, scale=scale)
+            ev[2].record()
+            attn_fwd(q, k[:, :, c:], v[:, :, c:], out=out_b, lse=lse_b, scale=scale)
+            ev[3].record()
+            attn_merge(out_a, lse_a, out_b, lse_b)
+            ev[4].record()
+
+        final_out, final_lse = out_a, lse_a
+        merge_rows = B * H * Sq
+        merge_bytes = merge_rows * (D * (4 + 4 + 4) + 12)
+        n_merge = 1
+    elif wl in ("qwen", "cosmos"):
+        out = torch.empty((B, H, Sq, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+        names = ["qk_norm_rope", "attn_fwd"]
+
+        def step(ev):
+            q.copy_(q0)
+            k.copy_(k0)
+            ev[0].record()
+            qk_norm_rope(q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
+            ev[1].record()
+            attn_fwd(q, k, v, out=out, lse=lse, scale=scale)
+            ev[2].record()
+
+        final_out, final_lse = out, lse
+        n_merge = 0
+    else:  # sp: one GPU's share of 4-way sequence parallelism
+        n = cfg.chunks
+        cs = Skv // n
+        outs = [torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev) for _ in range(n)]
+        lses = [torch.empty((B, H, Sq), dtype=torch.float32, device=dev) for _ in range(n)]
+        names = ["attn_fwd"] * n + ["attn_merge"] * (n - 1)
+
+        def step(ev):
+            i_ev = 0
+            ev[i_ev].record()
+            for i in range(n):
+                attn_fwd(q0, k0[:, :, i * cs:(i + 1) * cs], v[:, :, i * cs:(i + 1) * cs], out=outs[i],
+                         lse=lses[i], scale=scale)
+                i_ev += 1
+                ev[i_ev].record()
+            for i in range(1, n):
+                attn_merge(outs[0], lses[0], outs[i], lses[i])
+                i_ev += 1
+                ev[i_ev].record()
+
+        final_out, final_lse = outs[0], lses[0]
+        merge_rows = B * H * Sq
+        merge_bytes = merge_rows * (D * (4 + 4 + 4) + 12)
+        n_merge = n - 1
+
+    n_ev = len(names) + 1
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]  # noqa: E731
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    evs = [mk() for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    log(f"[bench] {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+
+    # Per-kernel durations (ms summed per step, averaged over steps).
+    per_kernel = {}
+    for ev in evs:
+        for j, nm in enumerate(names):
+            per_kernel.setdefault(nm, []).append(ev[j].elapsed_time(ev[j + 1]))
+    launches = {nm: names.count(nm) for nm in set(names)}
+
+    attn_flops = cfg.flops()
+    attn_ms_total = sum(per_kernel["attn_fwd"]) / args.steps          # per step
+    attn_launch_ms = attn_ms_total / launches["attn_fwd"]
+    attn_tflops = attn_flops / (attn_ms_total * 1e-3) / 1e12
+    kernels["attn_fwd"] = {"launches_per_step": launches["attn_fwd"], "avg_ms": round(attn_launch_ms, 4),
+                           "flop_per_step": attn_flops, "tflops": round(attn_tflops, 2),
+                           "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}
+    if "qk_norm_rope" in per_kernel:
+        pro_ms = sum(per_kernel["qk_norm_rope"]) / args.steps
+        pro_bytes = 2 * (2 + 2) * B * H * S * D + 2 * S * D * 4
+        kernels["qk_norm_rope"] = {"avg_ms": round(pro_ms, 4), "bytes": pro_bytes,
+                                   "gbs": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+                                   "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if n_merge:
+        mer_ms = sum(per_kernel["attn_merge"]) / args.steps / n_merge
+        kernels["attn_merge"] = {"launches_per_step": n_merge, "avg_ms": round(mer_ms, 4), "bytes": merge_bytes,
+                                 "gbs": round(merge_bytes / (mer_ms * 1e-3) / 1e9, 1),
+                                 "frac_hbm_peak": round(merge_bytes / (mer_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    value = attn_flops / (ms_per_step * 1e-3) / 1e12
+    flop_per_launch = attn_flops / launches["attn_fwd"]
+    roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                "flop_per_launch": flop_per_launch, "traffic": traffic_entry("attn_fwd", wl)}
+
+    workload_name = {
+        "wan": "Wan2.2-shaped attention step B1 H40 S75600 D128: QK RMSNorm+3D RoPE, ring-overlap "
+               "attention (local 1/4 + remote 3/4 of the keys), fp32 LSE merge",
+        "qwen": "Qwen-Image joint attention B1 H24 S4312 D128: QK RMSNorm+RoPE, attention",
+        "cosmos": "Cosmos-Predict video attention B2 H16 S12480 D128: QK RMSNorm+3D RoPE, attention",
+        "sp": "Wan2.2 4-way SP share: Sq 18900 x Skv 75600 H40 D128 as 4 KV chunks + 3 fp32 merges",
+    }[wl]
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 tensors; RMSNorm weights U(0.5,1.5))",
+        "config": {"workload": workload_name, "B": B, "H": H, "Sq": Sq, "Skv": Skv, "D": D,
+                   "causal": False, "scale": scale},
+        "roofline": roofline, "kernels": kernels,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle import compare
+        rows = inputs.sample_rows(cfg.index, B, H, Sq, per_head=64)
+        log(f"[bench] cpu baseline: oracle on {rows.size} rows")
+        if wl == "sp":
+            q_bits, k_bits = x["q"], x["k"]
+        else:
+            q_bits = q.cpu().view(torch.int16).numpy().view(np.uint16)
+            k_bits = k.cpu().view(torch.int16).numpy().view(np.uint16)
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        ref_o, ref_l = oracle.attn(q_bits, k_bits, x["v"], scale, False, rows=rows, nthreads=threads)
+        t_cpu = time.perf_counter() - t0
+        cpu_tflops = rows.size * 4.0 * Skv * D / t_cpu / 1e12
+        idx = torch.from_numpy(rows).to(dev)
+        got_o = final_out.reshape(-1, D).index_select(0, idx).double().cpu().numpy()
+        got_l = final_lse.reshape(-1).index_select(0, idx).double().cpu().numpy()
+        rep = compare.attn_report(got_o, ref_o, got_l, ref_l, bf16=final_out.dtype == torch.bfloat16)
+        result["cpu_baseline"] = {
+            "value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows.size} query rows (64 per (b,h)) of the measured workload against all "
+                      f"{Skv} keys, fp64 two-pass softmax, {t_cpu:.1f} s; prologue and merge not timed",
+            "seconds": round(t_cpu, 2)}
+        result["oracle_match"] = {k2: (round(v2, 8) if isinstance(v2, float) else v2) for k2, v2 in rep.items()}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

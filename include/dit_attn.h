@@ -1,0 +1,146 @@
+/*
+ * dit_attn.h -- C ABI of libdit_attn.so, the MI355X (gfx950) attention hot
+ * path of video and image diffusion transformers:
+ *
+ *   qk_norm_rope   per-head RMSNorm of q and k, then interleaved rotary, in place
+ *   attn_fwd       softmax(scale * Q K^T) V with a per-row log-sum-exp (BNSD)
+ *   attn_merge     fold of two partial attentions over disjoint key sets
+ *
+ * Sources of the operations (page title, section):
+ *   [COSMOS] "Cosmos 昇腾 NPU 多卡并行优化说明": §3.1 fused attention on BNSD
+ *            tensors with an explicit scale and a causal switch; §3.2 RMSNorm;
+ *            §3.3 rotary embedding.
+ *   [WAN]    "NPU Wan2.2-I2V模型推理优化实践": npu_fused_infer_attention_score
+ *            section (BNSD, softmax scale, non-causal/causal), rotary_mul
+ *            section (interleave mode), rms_norm section, Ring Attention
+ *            Overlap (two attention outputs merged through their LSE).
+ *   [PR274]  "feat: support Ascend NPU backend (torch_npu) for Qwen-Image
+ *            pipelines - #274": change list item 2 (ring attention folds
+ *            chunk results with update_out_and_lse).
+ *
+ * Conventions shared by every call
+ *   - Tensors are contiguous row-major device buffers.  BNSD means
+ *     q [B,H,Sq,D], k and v [B,H,Skv,D], out [B,H,Sq,D]; lse is fp32 [B,H,Sq].
+ *   - bf16 is IEEE bfloat16; conversions to it round to nearest even.
+ *   - D must be 64 or 128.  All sizes must be >= 1.  Offsets are 64-bit.
+ *   - Tensor pointers must be 16-byte aligned; lse pointers 4-byte aligned.
+ *   - The caller owns every buffer.  The library allocates nothing, frees
+ *     nothing, never synchronises, prints nothing and keeps no mutable
+ *     global state; calls are thread-safe and reentrant.
+ *   - Each call validates its arguments, then only enqueues work on
+ *     `stream` (NULL = the default stream) and returns.  Buffers must stay
+ *     alive until that work completes.  Invalid arguments are reported
+ *     before anything is launched; there is no fallback path of any kind.
+ *   - Return value: a dit_attn_status code.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same declaration as HIP's own; a caller may pass any hipStream_t. */
+typedef struct ihipStream_t *hipStream_t;
+
+enum dit_attn_status {
+    DIT_OK = 0,
+    DIT_ERR_NULL = 1,        /* a required pointer is NULL */
+    DIT_ERR_SHAPE = 2,       /* a size is < 1, or sizes are inconsistent/overflow */
+    DIT_ERR_UNSUPPORTED = 3, /* D not in {64,128}, or an unknown dtype code */
+    DIT_ERR_ALIGN = 4,       /* a pointer or stride breaks the alignment rule */
+    DIT_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
+    DIT_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+};
+
+enum dit_attn_dtype {
+    DIT_BF16 = 0,
+    DIT_FP32 = 1
+};
+
+/*
+ * Per-head RMSNorm followed by interleaved rotary embedding, in place.
+ * [COSMOS] §3.2 and [WAN] rms_norm: for every (b,h,s) row x of q (weight
+ * w_q) and of k (weight w_k), y_d = x_d / sqrt(mean_d x_d^2 + eps) * w_d.
+ * [COSMOS] §3.3 and [WAN] rotary_mul (interleave): adjacent pairs rotate with
+ * the tables taken elementwise at (s, d):
+ *   z_{2i}   = y_{2i}   cos[s,2i]   - y_{2i+1} sin[s,2i]
+ *   z_{2i+1} = y_{2i+1} cos[s,2i+1] + y_{2i}   sin[s,2i+1]
+ * Arithmetic in fp32; one rounding to bf16 at the end.
+ *
+ *   q, k      bf16 [B,H,S,D], read and overwritten.  Either may be NULL to
+ *             leave that tensor alone (not both); they must not overlap.
+ *   w_q, w_k  fp32 [D]; required exactly when q (resp. k) is given.
+ *   cos, sin  fp32 [S,D], shared by every (b,h) and by q and k.  To rotate a
+ *             slice of a longer sequence, pass the table rows of that slice.
+ *   eps       added to the mean square (>= 0 and finite).
+ */
+int qk_norm_rope(void *q, void *k, const float *w_q, const float *w_k,
+                 const float *cos, const float *sin, float eps,
+                 int B, int H, int S, int D, hipStream_t stream);
+
+/*
+ * Flash attention forward with per-row LSE.  [COSMOS] §3.1 and [WAN]
+ * npu_fused_infer_attention_score: for each (b,h) and query row i,
+ *   s_j = scale * q_i . k_j,  O_i = sum_j softmax_j(s) v_j,
+ *   lse_i = ln sum_j exp(s_j)   (natural log, of the scaled logits)
+ * over all keys j < Skv (causal = 0), or over j <= i (causal = 1: top-left
+ * aligned, so row i >= Skv sees every key).  Q K^T is a bf16 MFMA product
+ * and P V an fp16 MFMA product (P rounded to fp16, V converted from bf16),
+ * both with fp32 accumulation; the softmax runs in fp32.
+ *
+ *   q          bf16 [B,H,Sq,D]
+ *   k, v       bf16 [B,H,Skv,D]; v must satisfy |v| <= 65504 (its fp16
+ *              conversion is exact for |v| in [2^-14, 65504]; smaller
+ *              magnitudes keep an absolute accuracy of 2^-25)
+ *   out        [B,H,Sq,D], bf16 (out_dtype = DIT_BF16) or fp32 (DIT_FP32);
+ *              must not overlap q, k, v or lse
+ *   lse        fp32 [B,H,Sq], or NULL to skip it
+ *   scale      any finite value (typically 1/sqrt(D))
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+             int B, int H, int Sq, int Skv, int D, float scale, int causal,
+             int out_dtype, hipStream_t stream);
+
+/*
+ * attn_fwd over keys that are a window of longer per-head K/V buffers: key j
+ * of head (b,h) is read at k + (b*H + h) * kv_bh_stride + j * D (same for v).
+ * This is how a key chunk [c0, c1) of a [B,H,S,D] tensor is passed without
+ * a copy (k + c0*D, v + c0*D, Skv = c1 - c0, kv_bh_stride = S*D), e.g. the
+ * local-chunk / remote-chunks split of [WAN] Ring Attention Overlap.
+ * kv_bh_stride >= Skv*D and a multiple of 8 elements.  Otherwise as attn_fwd.
+ */
+int attn_fwd_kv_strided(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
+                        void *out, float *lse, int B, int H, int Sq, int Skv, int D,
+                        float scale, int causal, int out_dtype, hipStream_t stream);
+
+/*
+ * Merge of two partial attentions over disjoint key sets, in place into
+ * (out_a, lse_a).  [WAN] Ring Attention Overlap, [PR274] item 2
+ * (update_out_and_lse).  Per row:
+ *   M = max(la, lb),  L = M + ln(exp(la - M) + exp(lb - M)),
+ *   out_a <- exp(la - L) out_a + exp(lb - L) out_b,  lse_a <- L.
+ * A row whose two LSEs are both -inf (no key seen) becomes out_a = 0,
+ * lse_a = -inf.  fp32 arithmetic; one rounding per call when out_a is bf16.
+ *
+ *   out_a   [B,H,Sq,D] of a_dtype (DIT_BF16 or DIT_FP32), read and written
+ *   lse_a   fp32 [B,H,Sq], read and written
+ *   out_b   [B,H,Sq,D] of b_dtype, read only; must not overlap out_a/lse_a
+ *   lse_b   fp32 [B,H,Sq], read only; must not overlap out_a/lse_a
+ */
+int attn_merge(void *out_a, float *lse_a, const void *out_b, const float *lse_b,
+               int B, int H, int Sq, int D, int a_dtype, int b_dtype, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *dit_attn_status_string(int status);
+
+/* Static version string of the library. */
+const char *dit_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

@@ -62,10 +62,12 @@ def _load():
 
 
 def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may use, at most 16."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _ptr(a: np.ndarray):

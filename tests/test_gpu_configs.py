@@ -1,0 +1,134 @@
+"""The five workloads at full size: GPU path against the fp64 oracle.
+
+The prologue is compared on every element.  Attention is compared on a
+seeded sample of query rows per (b,h) (rows 0, 127, 128, the ragged tail,
+the last row and uniform draws), with the oracle consuming the GPU
+prologue's bf16 output, so stage errors do not compound.  Config 5 checks
+the 4-chunk ring chain with an fp32 accumulator and with bf16 chunk outputs
+and accumulator, and the all-gather path (Skv = 75600 in one call).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import compare
+from attention_qk_norm_rope_amd import attn_fwd, attn_merge, inputs, qk_norm_rope
+from gpu_common import dev_bits, dev_f32, host_bits, host_f64, rows_of, say, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _prologue(cfg, x):
+    cos, sin = inputs.config_rope_tables(cfg)
+    dq, dk = dev_bits(x["q"]), dev_bits(x["k"])
+    say(f"[config {cfg.index}] prologue")
+    qk_norm_rope(dq, dk, dev_f32(x["w_q"]), dev_f32(x["w_k"]), dev_f32(cos), dev_f32(sin), cfg.eps)
+    torch.cuda.synchronize()
+    return dq, dk, cos, sin
+
+
+def _check_prologue_heads(cfg, x, dq, dk, cos, sin, heads=None):
+    for got, src, w, name in ((dq, x["q"], x["w_q"], "q"), (dk, x["k"], x["w_k"], "k")):
+        if heads is None:
+            ref = oracle.qk_norm_rope(src, w, cos, sin, cfg.eps)
+            out = host_f64(got)
+        else:
+            ref = oracle.qk_norm_rope(np.ascontiguousarray(src[:, heads]), w, cos, sin, cfg.eps)
+            out = host_f64(got[:, heads])
+        rep = compare.prologue_report(out, ref)
+        say(f"[config {cfg.index}] prologue {name}: {rep}")
+        compare.assert_ok(rep, f"config {cfg.index} prologue {name}")
+
+
+def _check_attn(cfg, q_bits, k_bits, v_bits, out, lse, tag):
+    rows = inputs.sample_rows(cfg.index, cfg.B, cfg.H, q_bits.shape[2])
+    say(f"[config {cfg.index}] oracle on {rows.size} rows ({tag})")
+    ref_o, ref_l = oracle.attn(q_bits, k_bits, v_bits, cfg.scale, False, rows=rows)
+    rep = compare.attn_report(rows_of(out, rows), ref_o, rows_of(lse, rows), ref_l,
+                              bf16=out.dtype == torch.bfloat16)
+    say(f"[config {cfg.index}] {tag}: {rep}")
+    compare.assert_ok(rep, f"config {cfg.index} {tag}")
+
+
+@pytest.mark.parametrize("index", [2, 3])
+def test_prologue_then_attention(index):
+    cfg = inputs.CONFIGS[index]
+    x = workload(index)
+    dq, dk, cos, sin = _prologue(cfg, x)
+    _check_prologue_heads(cfg, x, dq, dk, cos, sin)
+    dv = dev_bits(x["v"])
+    say(f"[config {index}] attn_fwd")
+    out, lse = attn_fwd(dq, dk, dv, scale=cfg.scale)
+    torch.cuda.synchronize()
+    _check_attn(cfg, host_bits(dq), host_bits(dk), x["v"], out, lse, "attention")
+
+
+@pytest.mark.parametrize("times_four", [False, True], ids=["plain", "q_x4"])
+def test_wan_attention(times_four):
+    cfg = inputs.CONFIGS[4]
+    x = workload(4)
+    qb = inputs.times_four_bits(x["q"]) if times_four else x["q"]
+    say(f"[config 4] attn_fwd {'q x4' if times_four else 'plain'}")
+    out, lse = attn_fwd(dev_bits(qb), dev_bits(x["k"]), dev_bits(x["v"]), scale=cfg.scale)
+    torch.cuda.synchronize()
+    _check_attn(cfg, qb, x["k"], x["v"], out, lse, "q x4" if times_four else "plain")
+
+
+def test_wan_ring_overlap_step():
+    """The measured step: prologue on q and k, attention over the local
+    quarter of the keys and over the remaining three quarters (windows of the
+    same tensors), fp32 outputs merged through their LSE."""
+    cfg = inputs.CONFIGS[4]
+    x = workload(4)
+    dq, dk, cos, sin = _prologue(cfg, x)
+    _check_prologue_heads(cfg, x, dq, dk, cos, sin, heads=[0, 17, 39])
+    dv = dev_bits(x["v"])
+    c = cfg.S // 4
+    say("[config 4] ring-overlap attention")
+    oa, la = attn_fwd(dq, dk[:, :, :c], dv[:, :, :c], scale=cfg.scale, out_dtype=torch.float32)
+    ob, lb = attn_fwd(dq, dk[:, :, c:], dv[:, :, c:], scale=cfg.scale, out_dtype=torch.float32)
+    attn_merge(oa, la, ob, lb)
+    torch.cuda.synchronize()
+    _check_attn(cfg, host_bits(dq), host_bits(dk), x["v"], oa, la, "ring-overlap step")
+
+
+def test_sp_share_chains():
+    cfg = inputs.CONFIGS[5]
+    x4 = workload(4)
+    q = np.ascontiguousarray(x4["q"][:, :, : cfg.Sq])
+    kc, vc = inputs.split_kv(x4["k"], cfg.chunks), inputs.split_kv(x4["v"], cfg.chunks)
+    dq = dev_bits(q)
+    results = {}
+    for acc_dtype in (torch.float32, torch.bfloat16):
+        acc_o = acc_l = None
+        for i in range(cfg.chunks):
+            say(f"[config 5] chunk {i} ({acc_dtype})")
+            o, l = attn_fwd(dq, dev_bits(kc[i]), dev_bits(vc[i]), scale=cfg.scale, out_dtype=acc_dtype)
+            if acc_o is None:
+                acc_o, acc_l = o, l
+            else:
+                attn_merge(acc_o, acc_l, o, l)
+                del o, l
+        torch.cuda.synchronize()
+        results[acc_dtype] = (acc_o, acc_l)
+    say("[config 5] gather path (all keys in one call)")
+    go, gl = attn_fwd(dq, dev_bits(x4["k"]), dev_bits(x4["v"]), scale=cfg.scale)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(cfg.index, cfg.B, cfg.H, cfg.Sq)
+    say(f"[config 5] oracle on {rows.size} rows")
+    ref_o, ref_l = oracle.attn(q, x4["k"], x4["v"], cfg.scale, False, rows=rows)
+    reps = {}
+    for name, (o, l) in (("fp32 chain", results[torch.float32]), ("bf16 chain", results[torch.bfloat16]),
+                         ("gather", (go, gl))):
+        reps[name] = compare.attn_report(rows_of(o, rows), ref_o, rows_of(l, rows), ref_l,
+                                         bf16=o.dtype == torch.bfloat16)
+        say(f"[config 5] {name}: {reps[name]}")
+    # The fp32 chain rounded once to bf16 at the end.
+    o32 = results[torch.float32][0].to(torch.bfloat16)
+    reps["fp32 chain, bf16-rounded"] = compare.attn_report(rows_of(o32, rows), ref_o)
+    say(f"[config 5] fp32 chain bf16-rounded: {reps['fp32 chain, bf16-rounded']}")
+    for name, rep in reps.items():
+        compare.assert_ok(rep, f"config 5 {name}")
+    # Rounding every chunk to bf16 costs accuracy, as the pages warn.
+    assert reps["bf16 chain"]["max_abs"] >= reps["fp32 chain"]["max_abs"]

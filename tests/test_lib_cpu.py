@@ -1,0 +1,134 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/dit_attn.h declares, and rejects bad arguments with the
+documented status before anything is launched.
+
+Every call here is meant to fail validation, so no HIP call is made and no
+pointer is dereferenced (fake, suitably aligned addresses are used).  Because
+a mistake in one of these cases would launch a kernel on fake addresses, the
+module refuses to run where a GPU is visible; the GPU suite covers the same
+status codes with real buffers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_attn.h")
+LIB = os.path.join(ROOT, "attention_qk_norm_rope_amd", "libdit_attn.so")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP = range(7)
+BF16, FP32 = 0, 1
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("fake-pointer validation tests run only where no GPU is visible")
+    if not os.path.exists(LIB):
+        from attention_qk_norm_rope_amd import build
+        build.build()
+    lib = ctypes.CDLL(LIB)
+    p, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.qk_norm_rope.argtypes = [p, p, p, p, p, p, f32, i32, i32, i32, i32, p]
+    lib.attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_fwd_kv_strided.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
+    lib.dit_attn_status_string.restype = ctypes.c_char_p
+    lib.dit_attn_version.restype = ctypes.c_char_p
+    return lib
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_merge",
+                          "dit_attn_status_string", "dit_attn_version"}, names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for s in range(7):
+        assert lib.dit_attn_status_string(s)
+    assert lib.dit_attn_status_string(99) == b"unknown status"
+    assert b"gfx950" in lib.dit_attn_version()
+
+
+# Fake device addresses far apart, 256-byte aligned.
+Q, K, V, O, L, W1, W2, C, S_ = (0x10_0000_0000 * (i + 1) for i in range(9))
+
+
+def attn(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=256, Skv=256, D=64, scale=0.125, causal=0, dt=BF16):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, causal, dt, None)
+
+
+def test_attn_fwd_rejections(lib):
+    assert attn(lib, q=None) == NULL
+    assert attn(lib, o=None) == NULL
+    assert attn(lib, Sq=0) == SHAPE
+    assert attn(lib, Skv=0) == SHAPE
+    assert attn(lib, B=0) == SHAPE
+    assert attn(lib, H=-1) == SHAPE
+    assert attn(lib, D=96) == UNSUP
+    assert attn(lib, D=256) == UNSUP
+    assert attn(lib, dt=2) == UNSUP
+    assert attn(lib, scale=float("inf")) == SHAPE
+    assert attn(lib, scale=float("nan")) == SHAPE
+    assert attn(lib, q=Q + 8) == ALIGN
+    assert attn(lib, o=O + 4) == ALIGN
+    assert attn(lib, lse=L + 2) == ALIGN
+    assert attn(lib, o=Q) == ALIAS                       # out on q
+    assert attn(lib, o=K + 32 * 1024) == ALIAS           # out inside k (k spans 64 KiB)
+    assert attn(lib, lse=O + 1024) == ALIAS              # lse inside out
+    assert attn(lib, B=1 << 16, H=1 << 16) == SHAPE      # B*H overflows int
+
+
+def test_attn_fwd_kv_strided_rejections(lib):
+    f = lib.attn_fwd_kv_strided
+    assert f(Q, K, V, 255 * 64, O, L, 1, 2, 256, 256, 64, 0.125, 0, BF16, None) == SHAPE  # stride < Skv*D
+    assert f(Q, K, V, 256 * 64 + 4, O, L, 1, 2, 256, 256, 64, 0.125, 0, BF16, None) == ALIGN
+    # A long stride makes k span into out.
+    assert f(Q, K, V, (O - K) // 2, O, L, 1, 2, 256, 256, 64, 0.125, 0, BF16, None) == ALIAS
+
+
+def test_qk_norm_rope_rejections(lib):
+    f = lib.qk_norm_rope
+    args = dict(q=Q, k=K, wq=W1, wk=W2, c=C, s=S_, eps=1e-6, B=1, H=2, S=256, D=64)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["wq"], a["wk"], a["c"], a["s"], a["eps"], a["B"], a["H"], a["S"], a["D"], None)
+
+    assert call(q=None, k=None) == NULL
+    assert call(wq=None) == NULL
+    assert call(c=None) == NULL
+    assert call(S=0) == SHAPE
+    assert call(eps=-1.0) == SHAPE
+    assert call(eps=float("nan")) == SHAPE
+    assert call(D=32) == UNSUP
+    assert call(q=Q + 2) == ALIGN
+    assert call(c=C + 4) == ALIGN
+    assert call(k=Q + 512) == ALIAS                      # q and k overlap
+    assert call(c=Q + 1024) == ALIAS                     # table inside q
+    assert call(q=None, wq=None, k=K, c=K) == ALIAS      # table on k
+
+
+def test_attn_merge_rejections(lib):
+    f = lib.attn_merge
+    assert f(None, L, V, W1, 1, 2, 256, 64, BF16, BF16, None) == NULL
+    assert f(O, L, V, W1, 1, 0, 256, 64, BF16, BF16, None) == SHAPE
+    assert f(O, L, V, W1, 1, 2, 256, 64, BF16, 3, None) == UNSUP
+    assert f(O, L, V, W1, 1, 2, 256, 48, BF16, BF16, None) == UNSUP
+    assert f(O + 8, L, V, W1, 1, 2, 256, 64, BF16, BF16, None) == ALIGN
+    assert f(O, L + 1, V, W1, 1, 2, 256, 64, BF16, BF16, None) == ALIGN
+    assert f(O, L, O + 4096, W1, 1, 2, 256, 64, BF16, BF16, None) == ALIAS
+    assert f(O, O + 1024, V, W1, 1, 2, 256, 64, BF16, BF16, None) == ALIAS
+    assert f(O, L, V, L, 1, 2, 256, 64, FP32, BF16, None) == ALIAS
