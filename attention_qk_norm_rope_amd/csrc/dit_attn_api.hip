@@ -69,6 +69,10 @@ int attn_fwd_kv_strided(const void* q, const void* k, const void* v, int64_t kv_
     const int64_t BH = (int64_t)B * H;
     const int64_t q_elems = BH * Sq * D;
     if (BH > 0x7FFFFFFF || q_elems > kMaxElems) return DIT_ERR_SHAPE;
+    // The kernel addresses one (b,h) slab of q/k/v with 32-bit buffer offsets
+    // (including up to three tiles of read-ahead past the end).
+    if ((int64_t)(Sq + 512) * D * 2 > 0x7FFFFFFF || (int64_t)(Skv + 512) * D * 2 > 0x7FFFFFFF)
+        return DIT_ERR_SHAPE;
     if (kv_bh_stride < (int64_t)Skv * D) return DIT_ERR_SHAPE;
     if (kv_bh_stride > kMaxElems || (BH - 1) * kv_bh_stride > kMaxElems) return DIT_ERR_SHAPE;
     if (kv_bh_stride % 8 != 0) return DIT_ERR_ALIGN;
