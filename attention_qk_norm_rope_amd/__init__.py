@@ -3,12 +3,13 @@ with per-row LSE, and the out/LSE merge of KV chunks, as hand-written HIP
 kernels for gfx950 behind a C ABI (libdit_attn.so).
 
 ``inputs`` (seeded synthetic workloads) imports without a GPU; the kernel
-wrappers (``qk_norm_rope``, ``attn_fwd``, ``attn_merge``) load the HIP
+wrappers (``qk_norm_rope``, ``attn_fwd``, ``attn_fwd_ws``, ``attn_merge``) load the HIP
 library on first use and raise if it is missing.
 """
 from __future__ import annotations
 
-__all__ = ["qk_norm_rope", "attn_fwd", "attn_merge", "status_string", "version", "library_path"]
+__all__ = ["qk_norm_rope", "attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_merge",
+           "status_string", "version", "library_path"]
 
 
 def __getattr__(name):

@@ -45,8 +45,11 @@ def _load():
     lib.qk_norm_rope.argtypes = [p, p, p, p, p, p, f32, i32, i32, i32, i32, p]
     lib.attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_kv_strided.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_fwd_ws.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.attn_fwd_workspace_bytes.restype = i64
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
-    for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_merge"):
+    for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_merge"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -145,14 +148,7 @@ def _kv_bh_stride(t, B, H, S, D) -> int | None:
     return s1
 
 
-def attn_fwd(q, k, v, out=None, lse=None, scale: float | None = None, causal: bool = False,
-             out_dtype=torch.bfloat16, return_lse: bool = True):
-    """softmax(scale * q k^T) v with per-row LSE (natural log), BNSD.
-
-    q: bf16 [B,H,Sq,D] contiguous.  k, v: bf16 [B,H,Skv,D], contiguous or
-    windows along S of longer per-head buffers (same strides for k and v).
-    Returns (out, lse); lse is None when return_lse is False and no lse given.
-    """
+def _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse):
     _need(q, "q", torch.bfloat16, q.device)
     dev = q.device
     _need(k, "k", torch.bfloat16, dev)
@@ -176,22 +172,59 @@ def attn_fwd(q, k, v, out=None, lse=None, scale: float | None = None, causal: bo
             raise ValueError("out must be contiguous [B,H,Sq,D]")
         if out.device != dev:
             raise ValueError("out is on another device")
-    code = _dtype_code(out)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", torch.float32, dev)
         if tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
             raise ValueError("lse must be contiguous fp32 [B,H,Sq]")
+    return (B, H, Sq, Skv, D), int(sk), float(scale), out, lse
+
+
+def attn_fwd(q, k, v, out=None, lse=None, scale: float | None = None, causal: bool = False,
+             out_dtype=torch.bfloat16, return_lse: bool = True):
+    """softmax(scale * q k^T) v with per-row LSE (natural log), BNSD.
+
+    q: bf16 [B,H,Sq,D] contiguous.  k, v: bf16 [B,H,Skv,D], contiguous or
+    windows along S of longer per-head buffers (same strides for k and v).
+    Returns (out, lse); lse is None when return_lse is False and no lse given.
+    """
+    (B, H, Sq, Skv, D), sk, scale, out, lse = _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse)
+    code = _dtype_code(out)
     lib = _load()
     if k.is_contiguous() and v.is_contiguous():
         st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, Skv, D,
-                          float(scale), 1 if causal else 0, code, _stream())
+                          scale, 1 if causal else 0, code, _stream())
         _check("attn_fwd", st)
     else:
-        st = lib.attn_fwd_kv_strided(_ptr(q), _ptr(k), _ptr(v), int(sk), _ptr(out), _ptr(lse), B, H,
-                                     Sq, Skv, D, float(scale), 1 if causal else 0, code, _stream())
+        st = lib.attn_fwd_kv_strided(_ptr(q), _ptr(k), _ptr(v), sk, _ptr(out), _ptr(lse), B, H,
+                                     Sq, Skv, D, scale, 1 if causal else 0, code, _stream())
         _check("attn_fwd_kv_strided", st)
+    return out, lse
+
+
+def attn_fwd_workspace_bytes(B: int, H: int, Skv: int, D: int) -> int:
+    """Bytes of device workspace attn_fwd_ws needs for these sizes."""
+    n = int(_load().attn_fwd_workspace_bytes(int(B), int(H), int(Skv), int(D)))
+    if n < 0:
+        raise ValueError(f"no workspace size for B={B} H={H} Skv={Skv} D={D}")
+    return n
+
+
+def attn_fwd_ws(q, k, v, workspace, out=None, lse=None, scale: float | None = None,
+                causal: bool = False, out_dtype=torch.bfloat16, return_lse: bool = True):
+    """attn_fwd with a caller-owned device workspace (a contiguous tensor of
+    at least attn_fwd_workspace_bytes(B, H, Skv, D) bytes, any dtype).  Same
+    results as attn_fwd, faster: V is first rewritten into the workspace in
+    the kernel's tile layout.  The workspace holds scratch afterwards."""
+    (B, H, Sq, Skv, D), sk, scale, out, lse = _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _load().attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), sk, _ptr(workspace), ws_bytes, _ptr(out),
+                             _ptr(lse), B, H, Sq, Skv, D, scale, 1 if causal else 0, _dtype_code(out),
+                             _stream())
+    _check("attn_fwd_ws", st)
     return out, lse
 
 

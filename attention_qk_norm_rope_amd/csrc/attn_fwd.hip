@@ -75,10 +75,12 @@ constexpr float LN2 = 0.69314718055994531f;
 constexpr float TAU = 8.0f;            // lazy-rescale threshold, log2 units
 constexpr int RSRC_WORD3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
 
-template <int D, int BN>
+template <int D, int BN, bool VPRE>
 struct Lds {
     static constexpr int K_ELEMS = BN * D;   // K tile, XOR-swizzled 16-byte slots
-    static constexpr int VROW = BN + 8;      // V^T tile row stride, elements (16 B pad)
+    // V^T tile: padded rows when staged through registers, or the prepared
+    // image (unpadded rows, XOR-swizzled 16-byte slots) when DMAed.
+    static constexpr int VROW = VPRE ? BN : BN + 8;
     static constexpr int V_ELEMS = D * VROW;
 };
 
@@ -118,13 +120,13 @@ __device__ __forceinline__ unsigned pick_pair_f16(const u32x4& a, const u32x4& b
     return pack_f16(fa, fb);
 }
 
-template <int D, int NQB, int BN, bool OUT_F32>
+template <int D, int NQB, int BN, bool OUT_F32, bool VPRE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256)))
 __attribute__((amdgpu_waves_per_eu(NQB == 1 ? 2 : 1, NQB == 1 ? 2 : 1)))
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, int64_t kv_bh_stride, void* __restrict__ out,
                 float* __restrict__ lse, int Sq, int Skv, float c, unsigned qsign, int causal,
-                int n_qtiles) {
+                int n_qtiles, const uint16_t* __restrict__ vws) {
     constexpr int QPW = 32 * NQB;       // query rows per wave
     constexpr int BM = WAVES * QPW;     // query rows per workgroup
     constexpr int DT = D / 16;          // MFMA k-steps of Q K^T
@@ -132,12 +134,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     constexpr int KB = BN / 32;         // 32-key blocks per tile
     constexpr int SL = D / 8;           // 16-byte slots per K row
     constexpr int KDMA = BN * D * 2 / 1024 / WAVES;  // 1 KB DMA chunks per wave per tile
-    constexpr int VROW = Lds<D, BN>::VROW;
+    constexpr int VROW = Lds<D, BN, VPRE>::VROW;
+    static_assert(!VPRE || BN == 64, "the prepared V image uses 64-key tiles");
     constexpr int VKG = BN / 4;         // 4-key groups per V tile
     static_assert(KDMA >= 1 && BN % 32 == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Lds<D, BN>::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][Lds<D, BN>::V_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][Lds<D, BN, VPRE>::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][Lds<D, BN, VPRE>::V_ELEMS];
 
     // XCD-contiguous remap of the workgroup id.
     const int nblk = gridDim.x, wid = blockIdx.x;
@@ -215,6 +218,20 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
     };
 
+    // Prepared V: tile j of this (b,h) is the LDS image at vws + (bh*n_vt + j)*BN*D;
+    // reads past the last tile return zeros.
+    const int n_vt = (Skv + BN - 1) / BN;
+    const __amdgpu_buffer_rsrc_t rvw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(VPRE ? vws + (int64_t)bh * n_vt * BN * D : v), (short)0, VPRE ? n_vt * BN * D * 2 : 0, RSRC_WORD3);
+    auto dma_v = [&](int kv0, int b) {
+#pragma unroll
+        for (int i = 0; i < KDMA; ++i) {
+            const int chunk = wave * KDMA + i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rvw, (lds_void*)(&Vt[b][chunk * 512]), 16,
+                                                     (kv0 * D + chunk * 512 + lane * 8) * 2, 0, 0, 0);
+        }
+    };
+
     // S^T = K Q^T for the keys in Ks[b]; K fragments are read one k-step ahead.
     auto kfrag = [&](int b, int kb, int t) {
         const int key = 32 * kb + n;
@@ -280,7 +297,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int b = j & 1;
         const int kv0 = j * BN;
         dma_k(kv0 + 2 * BN, b);        // K_{j+2} (zeros past the end)
-        load_v(kv0 + BN);              // V_{j+1}
+        if constexpr (VPRE) dma_v(kv0 + BN, b ^ 1);   // V_{j+1} -> the buffer tile j-1 used
+        else load_v(kv0 + BN);                         // V_{j+1}
         qk(b ^ 1, sn);                 // S_{j+1}: MFMAs overlap the softmax below
 
         // ---- online softmax of tile j (one query per lane) ----
@@ -341,6 +359,11 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             constexpr int NV = KB * 2 * DB;
             auto vfrag = [&](int idx) {
                 const int kb = idx / (2 * DB), u = (idx / DB) % 2, db = idx % DB;
+                if constexpr (VPRE) {
+                    const int lslot = 4 * kb + 2 * u + hh;
+                    return __builtin_bit_cast(
+                        f16x8, *(const u32x4*)(&Vt[b][(32 * db + n) * VROW + 8 * (lslot ^ (n & 7))]));
+                }
                 return __builtin_bit_cast(
                     f16x8, *(const u32x4*)(&Vt[b][(32 * db + n) * VROW + 32 * kb + 16 * u + 8 * hh]));
             };
@@ -356,7 +379,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             }
         }
 
-        store_v(b ^ 1);                 // V_{j+1} -> the buffer tile j-1 used
+        if constexpr (!VPRE) store_v(b ^ 1);           // V_{j+1} -> the buffer tile j-1 used
         if (needs_mask(kv0 + BN)) mask(kv0 + BN, sn);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K_{j+2} has landed in LDS
         __syncthreads();
@@ -366,8 +389,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     f32x16 sA[KB][NQB], sB[KB][NQB];
     dma_k(0, 0);
     dma_k(BN, 1);
-    load_v(0);
-    store_v(0);
+    if constexpr (VPRE) {
+        dma_v(0, 0);
+    } else {
+        load_v(0);
+        store_v(0);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     qk(0, sA);
@@ -410,33 +437,36 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
 }
 
-template <int D, int NQB, int BN, bool OUT_F32>
+template <int D, int NQB, int BN, bool OUT_F32, bool VPRE>
 hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out,
                   float* lse, int BH, int Sq, int Skv, float c, unsigned qsign, bool causal,
-                  hipStream_t stream) {
+                  const void* vws, hipStream_t stream) {
     constexpr int BM = WAVES * 32 * NQB;
     const int n_qtiles = (Sq + BM - 1) / BM;
     const int64_t nblk = (int64_t)n_qtiles * BH;
     if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NQB, BN, OUT_F32>), dim3((unsigned)nblk), dim3(256), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, kv_bh_stride, out,
-                       lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NQB, BN, OUT_F32, VPRE>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, kv_bh_stride,
+                       out, lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, (const uint16_t*)vws);
     return hipGetLastError();
 }
 
 template <int D, bool OUT_F32>
 hipError_t launch_d(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out,
                     float* lse, int BH, int Sq, int Skv, float c, unsigned qsign, bool causal,
-                    hipStream_t stream) {
-    return launch<D, ATTN_NQB, ATTN_BN, OUT_F32>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal,
-                                                 stream);
+                    const void* vws, hipStream_t stream) {
+    if (vws)
+        return launch<D, ATTN_NQB, 64, OUT_F32, true>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign,
+                                                      causal, vws, stream);
+    return launch<D, ATTN_NQB, ATTN_BN, OUT_F32, false>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign,
+                                                        causal, nullptr, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int Sq, int Skv, int D, float scale,
-                           bool causal, bool out_f32, hipStream_t stream) {
+                           bool causal, bool out_f32, const void* vws, hipStream_t stream) {
     // Positive multiplier for exp2; the sign of the scale goes into Q.  A
     // zero (or vanishing) scale keeps a tiny positive multiplier so that
     // masked logits (-inf) still map to probability 0; the logits it yields
@@ -445,11 +475,11 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
     if (!(c >= 1e-30f)) c = 1e-30f;
     const unsigned qsign = scale < 0.f ? 0x80008000u : 0u;
     if (D == 128) {
-        return out_f32 ? launch_d<128, true>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, stream)
-                       : launch_d<128, false>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, stream);
+        return out_f32 ? launch_d<128, true>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, vws, stream)
+                       : launch_d<128, false>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, vws, stream);
     }
-    return out_f32 ? launch_d<64, true>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, stream)
-                   : launch_d<64, false>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, stream);
+    return out_f32 ? launch_d<64, true>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, vws, stream)
+                   : launch_d<64, false>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, vws, stream);
 }
 
 }  // namespace dit

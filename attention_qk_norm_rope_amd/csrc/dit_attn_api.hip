@@ -58,9 +58,18 @@ int qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k, const flo
                                                eps, (int)BH, S, D, stream));
 }
 
-int attn_fwd_kv_strided(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out,
-                        float* lse, int B, int H, int Sq, int Skv, int D, float scale, int causal,
-                        int out_dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks of the attention entry points; on success fills
+// the byte ranges of every tensor for the alias checks.
+struct AttnRanges {
+    Range q, k, v, out, lse;
+};
+
+int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
+               int B, int H, int Sq, int Skv, int D, float scale, int out_dtype, AttnRanges* r) {
     if (!q || !k || !v || !out) return DIT_ERR_NULL;
     if (B < 1 || H < 1 || Sq < 1 || Skv < 1 || D < 1) return DIT_ERR_SHAPE;
     if (!isfinite(scale)) return DIT_ERR_SHAPE;
@@ -79,14 +88,58 @@ int attn_fwd_kv_strided(const void* q, const void* k, const void* v, int64_t kv_
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
         return DIT_ERR_ALIGN;
     const int64_t kv_elems = (BH - 1) * kv_bh_stride + (int64_t)Skv * D;
-    const Range rq = range_of(q, q_elems * 2), rk = range_of(k, kv_elems * 2), rv = range_of(v, kv_elems * 2);
-    const Range ro = range_of(out, q_elems * (out_dtype == DIT_FP32 ? 4 : 2));
-    const Range rl = range_of(lse, lse ? BH * Sq * 4 : 0);
-    if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return DIT_ERR_ALIAS;
-    if (lse && (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ro))) return DIT_ERR_ALIAS;
+    r->q = range_of(q, q_elems * 2);
+    r->k = range_of(k, kv_elems * 2);
+    r->v = range_of(v, kv_elems * 2);
+    r->out = range_of(out, q_elems * (out_dtype == DIT_FP32 ? 4 : 2));
+    r->lse = range_of(lse, lse ? BH * Sq * 4 : 0);
+    if (overlap(r->out, r->q) || overlap(r->out, r->k) || overlap(r->out, r->v)) return DIT_ERR_ALIAS;
+    if (lse && (overlap(r->lse, r->q) || overlap(r->lse, r->k) || overlap(r->lse, r->v) || overlap(r->lse, r->out)))
+        return DIT_ERR_ALIAS;
+    return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_kv_strided(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out,
+                        float* lse, int B, int H, int Sq, int Skv, int D, float scale, int causal,
+                        int out_dtype, hipStream_t stream) {
+    AttnRanges r;
+    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Sq, Skv, D, scale, out_dtype, &r);
+    if (st != DIT_OK) return st;
     (void)hipGetLastError();
-    return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, (int)BH, Sq, Skv, D, scale,
-                                           causal != 0, out_dtype == DIT_FP32, stream));
+    return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, Sq, Skv, D, scale,
+                                           causal != 0, out_dtype == DIT_FP32, nullptr, stream));
+}
+
+int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D) {
+    if (B < 1 || H < 1 || Skv < 1 || (D != 64 && D != 128)) return -1;
+    const int64_t BH = (int64_t)B * H;
+    if (BH > 0x7FFFFFFF || (int64_t)(Skv + 512) * D * 2 > 0x7FFFFFFF) return -1;
+    return dit::v_prep_bytes(BH, Skv, D);
+}
+
+int attn_fwd_ws(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
+                int64_t workspace_bytes, void* out, float* lse, int B, int H, int Sq, int Skv, int D,
+                float scale, int causal, int out_dtype, hipStream_t stream) {
+    AttnRanges r;
+    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Sq, Skv, D, scale, out_dtype, &r);
+    if (st != DIT_OK) return st;
+    if (!workspace) return DIT_ERR_NULL;
+    if (!aligned(workspace, 16)) return DIT_ERR_ALIGN;
+    const int64_t need = attn_fwd_workspace_bytes(B, H, Skv, D);
+    if (need < 0 || workspace_bytes < need) return DIT_ERR_SHAPE;
+    const Range rw = range_of(workspace, need);
+    if (overlap(rw, r.q) || overlap(rw, r.k) || overlap(rw, r.v) || overlap(rw, r.out) ||
+        (lse && overlap(rw, r.lse)))
+        return DIT_ERR_ALIAS;
+    (void)hipGetLastError();
+    hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * H, Skv, D, stream);
+    if (e != hipSuccess) return DIT_ERR_HIP;
+    return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, Sq, Skv, D, scale,
+                                           causal != 0, out_dtype == DIT_FP32, workspace, stream));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Sq,

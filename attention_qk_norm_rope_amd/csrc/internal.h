@@ -7,10 +7,16 @@
 
 namespace dit {
 
-// Attention: q [BH,Sq,D] bf16; k/v rows at k + bh*kv_bh_stride + j*D.
+// Attention: q [BH,Sq,D] bf16; k/v rows at k + bh*kv_bh_stride + j*D.  With
+// vws != null, V is read from the prepared tiles written by launch_v_prep.
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int Sq, int Skv, int D, float scale,
-                           bool causal, bool out_f32, hipStream_t stream);
+                           bool causal, bool out_f32, const void* vws, hipStream_t stream);
+
+// Bytes of prepared V for BH heads of Skv keys; launch_v_prep writes them.
+int64_t v_prep_bytes(int64_t BH, int Skv, int D);
+hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D,
+                         hipStream_t stream);
 
 // RMSNorm + interleaved rotary, in place; q or k may be null.
 hipError_t launch_qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k,

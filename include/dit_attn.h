@@ -117,6 +117,30 @@ int attn_fwd_kv_strided(const void *q, const void *k, const void *v, int64_t kv_
                         float scale, int causal, int out_dtype, hipStream_t stream);
 
 /*
+ * attn_fwd_kv_strided (same arguments and results) with a caller-provided
+ * workspace that lets the kernel stream V without converting it: a first
+ * launch writes each 64-key tile of V once as an fp16, transposed tile image
+ * into `workspace`, and the attention launch copies those images straight
+ * into LDS.  Faster than attn_fwd on the same inputs; the results are the
+ * same arithmetic (identical bits).
+ *
+ *   workspace        device buffer of at least attn_fwd_workspace_bytes(B, H,
+ *                    Skv, D) bytes, 16-byte aligned, overlapping no other
+ *                    argument.  Its contents are scratch: overwritten by
+ *                    every call, meaningless afterwards.  Calls that share a
+ *                    workspace must be ordered on one stream.
+ *   workspace_bytes  its size (DIT_ERR_SHAPE when too small)
+ */
+int attn_fwd_ws(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
+                void *workspace, int64_t workspace_bytes, void *out, float *lse,
+                int B, int H, int Sq, int Skv, int D, float scale, int causal,
+                int out_dtype, hipStream_t stream);
+
+/* Workspace bytes attn_fwd_ws needs (B*H * ceil(Skv/64) * 64 * D * 2), or -1
+ * for arguments attn_fwd_ws would reject. */
+int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D);
+
+/*
  * Merge of two partial attentions over disjoint key sets, in place into
  * (out_a, lse_a).  [WAN] Ring Attention Overlap, [PR274] item 2
  * (update_out_and_lse).  Per row:

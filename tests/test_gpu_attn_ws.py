@@ -1,0 +1,85 @@
+"""attn_fwd_ws (V rewritten once into a caller workspace, then streamed into
+LDS by DMA) on the GPU: the same results as attn_fwd, bit for bit, and the
+oracle's within the parity tolerances, on the attention cases of the plain
+path plus key windows, D = 64 and a reused workspace."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import compare
+from attention_qk_norm_rope_amd import attn_fwd, attn_fwd_ws, attn_fwd_workspace_bytes, inputs
+from attention_qk_norm_rope_amd.binding import DitAttnError
+from gpu_common import DEV, dev_bits, host_f64, say
+from test_gpu_attn import CASES, _ids
+
+pytestmark = pytest.mark.gpu
+
+
+def _ws(B, H, Skv, D, fill=0x7E):
+    n = attn_fwd_workspace_bytes(B, H, Skv, D)
+    # Filled with garbage (fp16 NaN patterns) so unread-before-written bytes would show.
+    return torch.full((n,), fill, dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
+def test_ws_matches_plain_and_oracle(case):
+    B, H, Sq, Skv, D, causal, scale, out_dtype = case
+    if scale is None:
+        scale = 1 / math.sqrt(D)
+    seed = Sq * 7 + Skv
+    q = inputs.random_bits(seed, (B, H, Sq, D))
+    k = inputs.random_bits(seed + 1, (B, H, Skv, D))
+    v = inputs.random_bits(seed + 2, (B, H, Skv, D))
+    dq, dk, dv = dev_bits(q), dev_bits(k), dev_bits(v)
+    say(f"[attn_ws] {_ids(case)}")
+    o1, l1 = attn_fwd_ws(dq, dk, dv, _ws(B, H, Skv, D), scale=scale, causal=causal, out_dtype=out_dtype)
+    o0, l0 = attn_fwd(dq, dk, dv, scale=scale, causal=causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+    ref_o, ref_l = oracle.attn(q, k, v, scale, causal)
+    rep = compare.attn_report(host_f64(o1), ref_o, host_f64(l1), ref_l, bf16=out_dtype == torch.bfloat16)
+    compare.assert_ok(rep, "ws " + _ids(case))
+
+
+def test_ws_on_key_windows_and_reuse():
+    """Windows of longer K/V (the strided layout), one workspace reused for
+    calls of decreasing size: every call equals attn_fwd bit for bit."""
+    B, H, S, Sq, D = 1, 3, 700, 300, 128
+    q = dev_bits(inputs.random_bits(71, (B, H, Sq, D)))
+    k = dev_bits(inputs.random_bits(72, (B, H, S, D)))
+    v = dev_bits(inputs.random_bits(73, (B, H, S, D)))
+    ws = _ws(B, H, S, D)
+    for a, b in ((0, 700), (175, 700), (64, 129), (0, 1)):
+        say(f"[attn_ws] window {a}:{b}")
+        ow, lw = attn_fwd_ws(q, k[:, :, a:b], v[:, :, a:b], ws, out_dtype=torch.float32)
+        oc, lc = attn_fwd(q, k[:, :, a:b], v[:, :, a:b], out_dtype=torch.float32)
+        assert torch.equal(ow, oc) and torch.equal(lw, lc), (a, b)
+
+
+def test_ws_large_logits_d64():
+    B, H, Sq, Skv, D = 2, 2, 333, 1111, 64
+    q = inputs.random_bits(81, (B, H, Sq, D), std=8.0)
+    k = inputs.random_bits(82, (B, H, Skv, D))
+    v = inputs.random_bits(83, (B, H, Skv, D))
+    say("[attn_ws] D64 std-8 logits")
+    out, lse = attn_fwd_ws(dev_bits(q), dev_bits(k), dev_bits(v), _ws(B, H, Skv, D), out_dtype=torch.float32)
+    ref_o, ref_l = oracle.attn(q, k, v, 1 / math.sqrt(D))
+    compare.assert_ok(compare.attn_report(host_f64(out), ref_o, host_f64(lse), ref_l, bf16=False), "ws D64")
+
+
+def test_ws_rejects_small_or_misplaced_workspace():
+    B, H, S, D = 1, 2, 256, 128
+    q = dev_bits(inputs.random_bits(91, (B, H, S, D)))
+    n = attn_fwd_workspace_bytes(B, H, S, D)
+    small = torch.empty((n - 16,), dtype=torch.uint8, device=DEV)
+    with pytest.raises(DitAttnError) as e:
+        attn_fwd_ws(q, q, q, small)
+    assert e.value.status == 2
+    with pytest.raises(DitAttnError) as e:            # workspace on top of the output
+        out = torch.empty((n // 2,), dtype=torch.bfloat16, device=DEV)
+        attn_fwd_ws(q, q, q, out, out=out[: B * H * S * D].view(B, H, S, D))
+    assert e.value.status == 5
+    np.testing.assert_equal(n, B * H * (S // 64) * 64 * D * 2)

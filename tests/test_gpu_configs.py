@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from oracle import compare
-from attention_qk_norm_rope_amd import attn_fwd, attn_merge, inputs, qk_norm_rope
+from attention_qk_norm_rope_amd import (attn_fwd, attn_fwd_workspace_bytes, attn_fwd_ws, attn_merge, inputs,
+                                        qk_norm_rope)
 from gpu_common import dev_bits, dev_f32, host_bits, host_f64, rows_of, say, workload
 
 pytestmark = pytest.mark.gpu
@@ -78,16 +79,24 @@ def test_wan_attention(times_four):
 def test_wan_ring_overlap_step():
     """The measured step: prologue on q and k, attention over the local
     quarter of the keys and over the remaining three quarters (windows of the
-    same tensors), fp32 outputs merged through their LSE."""
+    same tensors, through the workspace path with one shared workspace), fp32
+    outputs merged through their LSE.  The local window is also run through
+    attn_fwd, which must give the same bits."""
     cfg = inputs.CONFIGS[4]
     x = workload(4)
     dq, dk, cos, sin = _prologue(cfg, x)
     _check_prologue_heads(cfg, x, dq, dk, cos, sin, heads=[0, 17, 39])
     dv = dev_bits(x["v"])
     c = cfg.S // 4
-    say("[config 4] ring-overlap attention")
-    oa, la = attn_fwd(dq, dk[:, :, :c], dv[:, :, :c], scale=cfg.scale, out_dtype=torch.float32)
-    ob, lb = attn_fwd(dq, dk[:, :, c:], dv[:, :, c:], scale=cfg.scale, out_dtype=torch.float32)
+    ws = torch.empty((attn_fwd_workspace_bytes(cfg.B, cfg.H, cfg.S - c, cfg.D),), dtype=torch.uint8,
+                     device=dq.device)
+    say("[config 4] ring-overlap attention (workspace path)")
+    oa, la = attn_fwd_ws(dq, dk[:, :, :c], dv[:, :, :c], ws, scale=cfg.scale, out_dtype=torch.float32)
+    op, lp = attn_fwd(dq, dk[:, :, :c], dv[:, :, :c], scale=cfg.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, op) and torch.equal(la, lp)
+    del op, lp
+    ob, lb = attn_fwd_ws(dq, dk[:, :, c:], dv[:, :, c:], ws, scale=cfg.scale, out_dtype=torch.float32)
     attn_merge(oa, la, ob, lb)
     torch.cuda.synchronize()
     _check_attn(cfg, host_bits(dq), host_bits(dk), x["v"], oa, la, "ring-overlap step")

@@ -41,6 +41,9 @@ def lib():
     lib.qk_norm_rope.argtypes = [p, p, p, p, p, p, f32, i32, i32, i32, i32, p]
     lib.attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_kv_strided.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_fwd_ws.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.attn_fwd_workspace_bytes.restype = i64
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
     lib.dit_attn_version.restype = ctypes.c_char_p
@@ -49,8 +52,9 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_merge",
-                          "dit_attn_status_string", "dit_attn_version"}, names
+    assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
+                          "attn_fwd_workspace_bytes", "attn_merge", "dit_attn_status_string",
+                          "dit_attn_version"}, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -97,6 +101,39 @@ def test_attn_fwd_kv_strided_rejections(lib):
     assert f(Q, K, V, 256 * 64 + 4, O, L, 1, 2, 256, 256, 64, 0.125, 0, BF16, None) == ALIGN
     # A long stride makes k span into out.
     assert f(Q, K, V, (O - K) // 2, O, L, 1, 2, 256, 256, 64, 0.125, 0, BF16, None) == ALIAS
+
+
+def test_attn_fwd_workspace_bytes(lib):
+    f = lib.attn_fwd_workspace_bytes
+    # One fp16 image of 64 keys x D per started 64-key tile and head.
+    assert f(1, 2, 256, 64) == 2 * 4 * 64 * 64 * 2
+    assert f(1, 1, 1, 128) == 64 * 128 * 2
+    assert f(2, 3, 65, 128) == 6 * 2 * 64 * 128 * 2
+    assert f(1, 40, 75600, 128) == 40 * 1182 * 64 * 128 * 2
+    assert f(0, 2, 256, 64) == -1
+    assert f(1, 2, 0, 64) == -1
+    assert f(1, 2, 256, 96) == -1
+
+
+WS = 0x10_0000_0000 * 12
+
+
+def test_attn_fwd_ws_rejections(lib):
+    f = lib.attn_fwd_ws
+    need = 2 * 4 * 64 * 64 * 2
+
+    def call(ws=WS, nbytes=need, k=K, stride=256 * 64, Skv=256, o=O):
+        return f(Q, k, V, stride, ws, nbytes, o, L, 1, 2, 256, Skv, 64, 0.125, 0, BF16, None)
+
+    assert call(ws=None) == NULL
+    assert call(ws=WS + 8) == ALIGN
+    assert call(nbytes=need - 1) == SHAPE
+    assert call(nbytes=0) == SHAPE
+    assert call(ws=Q + 4096) == ALIAS                    # workspace inside q
+    assert call(ws=O - need + 16) == ALIAS               # workspace runs into out
+    assert call(ws=L) == ALIAS                           # workspace on lse
+    assert call(o=None) == NULL                          # the attention checks come first
+    assert call(stride=255 * 64) == SHAPE
 
 
 def test_qk_norm_rope_rejections(lib):
