@@ -60,6 +60,14 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    # A kernel whose host-side launch stub the compiler dropped would leave
+    # an undefined __device_stub__ symbol that only fails at load time.
+    nm = shutil.which("nm")
+    if nm:
+        syms = subprocess.run([nm, "-u", tmp], capture_output=True, text=True).stdout
+        missing = [l.split()[-1] for l in syms.splitlines() if "__device_stub__" in l]
+        if missing:
+            raise RuntimeError(f"undefined kernel launch stubs in {tmp}: {missing}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -6,9 +6,10 @@
 // Tile image (64 keys x D rows of 128 bytes): row d holds the 64 keys of
 // dimension d as fp16, keys in the order vt_col (bits 2 and 3 of the key
 // index swapped, which matches the MFMA accumulator's row order), split in 8
-// slots of 16 bytes stored at slot ^ (d % 8) (bank-conflict-free fragment
-// reads).  Keys past Skv are zero.  HBM-bound: reads 2 B and writes 2 B per
-// element of V (plus the zero tail of the last tile).
+// slots of 16 bytes; slot l is stored at l ^ ((d >> 1) & 7), so the 16 lanes
+// that read one slot of 16 consecutive rows hit distinct 16-byte groups of a
+// 256-byte LDS bank line.  Keys past Skv are zero.  HBM-bound: reads 2 B and
+// writes 2 B per element of V (plus the zero tail of the last tile).
 #include "internal.h"
 
 namespace dit {
@@ -63,7 +64,7 @@ v_prep_kernel(const uint16_t* __restrict__ v, int64_t kv_bh_stride, uint16_t* __
             for (int e = 0; e < 8; ++e) {
                 const int d = 8 * dc + e;
                 const u32x2 w = {pick_pair_f16(r[0], r[1], e), pick_pair_f16(r[2], r[3], e)};
-                *(u32x2*)(&img[d * BN + 8 * (lslot ^ (d & 7)) + sub]) = w;
+                *(u32x2*)(&img[d * BN + 8 * (lslot ^ ((d >> 1) & 7)) + sub]) = w;
             }
         }
         __syncthreads();
