@@ -93,7 +93,7 @@ hipError_t launch(void* out_a, float* lse_a, const void* out_b, const float* lse
                   hipStream_t stream) {
     constexpr int RPB = 256 / (D / 8);
     int64_t blocks = (rows + RPB - 1) / RPB;
-    if (blocks > 16384) blocks = 16384;
+    if (blocks > (1 << 18)) blocks = 1 << 18;   // grid-stride beyond 2^18 blocks
     hipLaunchKernelGGL((attn_merge_kernel<D, AF32, BF32>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        out_a, lse_a, out_b, lse_b, rows);
     return hipGetLastError();

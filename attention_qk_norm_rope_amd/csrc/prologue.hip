@@ -28,11 +28,11 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 
 // Grid: x = blocks of RPB sequence positions, y = q or k, z = groups of HB
 // heads.  A thread loads the cos/sin/weight values of its row slice once and
-// applies them to the same position of HB heads (4 rows in flight), so the
+// applies them to the same position of HB heads (8 rows in flight), so the
 // tables (shared by every (b,h)) are read once per HB heads instead of once
 // per row.
-constexpr int HB = 16;       // (b,h) rows per thread
-constexpr int UNR = 4;       // rows in flight per thread
+constexpr int HB = 40;       // (b,h) rows per thread
+constexpr int UNR = 8;       // rows in flight per thread
 
 template <int D>
 __global__ void __launch_bounds__(256)

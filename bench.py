@@ -56,7 +56,25 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan", choices=["wan", "qwen", "cosmos", "sp"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain device copies of a known size (the reference for rocprofv3's "
+                         "FETCH_SIZE/WRITE_SIZE counters) and print their byte counts")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """Three device-to-device copies of 1 GiB each: every copy reads and
+    writes exactly 2^30 bytes, so FETCH_SIZE/WRITE_SIZE of the copy kernel
+    give the counters' scale."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy": {"bytes_read": n, "bytes_written": n, "copies": 3}}), flush=True)
 
 
 def traffic_entry(kernel: str, workload: str):
@@ -79,6 +97,9 @@ def traffic_entry(kernel: str, workload: str):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
