@@ -245,3 +245,43 @@ def attn_merge(out_a, lse_a, out_b, lse_b):
                             _dtype_code(out_a), _dtype_code(out_b), _stream())
     _check("attn_merge", st)
     return out_a, lse_a
+
+
+def attn_fwd_ring_overlap(q, k, v, split: int, ws_local, ws_remote, out_local=None, lse_local=None,
+                          out_remote=None, lse_remote=None, scale: float | None = None,
+                          side_stream=None):
+    """The ring-overlap split on one GPU: attention of q over the keys
+    [0, split) ("local") and over [split, Skv) ("remote"), merged through the
+    LSE into fp32 (out_local, lse_local), which are returned.
+
+    With a side_stream (a torch.cuda.Stream of default priority) the local
+    call runs on it, concurrently with the remote call on the current stream;
+    the current stream waits for both before the merge.  Without one, both
+    run in order on the current stream.  Each call needs its own workspace
+    (attn_fwd_workspace_bytes of its key count) when they run concurrently.
+    Non-causal only (a key split has no causal offset).
+    """
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if not 0 < split < Skv:
+        raise ValueError(f"split must be in (0, {Skv})")
+    if side_stream is not None and ws_local.data_ptr() == ws_remote.data_ptr():
+        raise ValueError("concurrent calls need two workspaces")
+    mk = lambda: torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device)  # noqa: E731
+    ml = lambda: torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)  # noqa: E731
+    out_local = mk() if out_local is None else out_local
+    lse_local = ml() if lse_local is None else lse_local
+    out_remote = mk() if out_remote is None else out_remote
+    lse_remote = ml() if lse_remote is None else lse_remote
+    main = torch.cuda.current_stream(q.device)
+    if side_stream is None:
+        attn_fwd_ws(q, k[:, :, :split], v[:, :, :split], ws_local, out=out_local, lse=lse_local, scale=scale)
+        attn_fwd_ws(q, k[:, :, split:], v[:, :, split:], ws_remote, out=out_remote, lse=lse_remote, scale=scale)
+    else:
+        side_stream.wait_stream(main)          # inputs written on the current stream
+        with torch.cuda.stream(side_stream):
+            attn_fwd_ws(q, k[:, :, :split], v[:, :, :split], ws_local, out=out_local, lse=lse_local, scale=scale)
+        attn_fwd_ws(q, k[:, :, split:], v[:, :, split:], ws_remote, out=out_remote, lse=lse_remote, scale=scale)
+        main.wait_stream(side_stream)
+    attn_merge(out_local, lse_local, out_remote, lse_remote)
+    return out_local, lse_local

@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan", choices=["wan", "qwen", "cosmos", "sp"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ring-streams", type=int, default=1, choices=[1, 2],
+                    help="wan workload: run the local and remote attention calls on one stream in order (1) "
+                         "or concurrently on two streams (2)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain device copies of a known size (the reference for rocprofv3's "
                          "FETCH_SIZE/WRITE_SIZE counters) and print their byte counts")
@@ -109,7 +112,8 @@ def main():
     import numpy as np
     import torch
 
-    from attention_qk_norm_rope_amd import attn_fwd_workspace_bytes, attn_fwd_ws, attn_merge, inputs, qk_norm_rope
+    from attention_qk_norm_rope_amd import (attn_fwd_ring_overlap, attn_fwd_workspace_bytes, attn_fwd_ws, attn_merge,
+                                            inputs, qk_norm_rope)
     from attention_qk_norm_rope_amd import binding
 
     if not torch.cuda.is_available():
@@ -150,7 +154,31 @@ def main():
         w_q = torch.from_numpy(x["w_q"]).to(dev)
         w_k = torch.from_numpy(x["w_k"]).to(dev)
 
-    if wl == "wan":
+    if wl == "wan" and args.ring_streams == 2:
+        # Local and remote calls concurrently on two streams (own workspaces);
+        # the attention interval spans both calls.
+        c = S // 4
+        out_a = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+        out_b = torch.empty_like(out_a)
+        lse_a = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+        lse_b = torch.empty_like(lse_a)
+        ws_local = torch.empty((attn_fwd_workspace_bytes(B, H, c, D),), dtype=torch.uint8, device=dev)
+        side = torch.cuda.Stream(device=dev)
+        names = ["qk_norm_rope", "attn_fwd+attn_merge"]
+
+        def step(ev):
+            q.copy_(q0)
+            k.copy_(k0)
+            ev[0].record()
+            qk_norm_rope(q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
+            ev[1].record()
+            attn_fwd_ring_overlap(q, k, v, c, ws_local, ws, out_local=out_a, lse_local=lse_a, out_remote=out_b,
+                                  lse_remote=lse_b, scale=scale, side_stream=side)
+            ev[2].record()
+
+        final_out, final_lse = out_a, lse_a
+        n_merge = 0
+    elif wl == "wan":
         c = S // 4
         out_a = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
         out_b = torch.empty_like(out_a)
@@ -246,11 +274,20 @@ def main():
     launches = {nm: names.count(nm) for nm in set(names)}
 
     attn_flops = cfg.flops()
-    attn_ms_total = sum(per_kernel["attn_fwd"]) / args.steps          # per step
-    attn_launch_ms = attn_ms_total / launches["attn_fwd"]
+    if "attn_fwd" in per_kernel:
+        attn_ms_total = sum(per_kernel["attn_fwd"]) / args.steps          # per step
+        n_attn = launches["attn_fwd"]
+        entry = "attn_fwd_ws (v_prep_kernel + attn_fwd_kernel per call)"
+    else:
+        # Two streams: the interval spans both overlapped calls and the merge.
+        attn_ms_total = sum(per_kernel["attn_fwd+attn_merge"]) / args.steps
+        n_attn = 2
+        entry = ("attn_fwd_ring_overlap: 2 attn_fwd_ws calls on two streams + attn_merge "
+                 "(avg_ms = overlapped span / 2)")
+    attn_launch_ms = attn_ms_total / n_attn
     attn_tflops = attn_flops / (attn_ms_total * 1e-3) / 1e12
-    kernels["attn_fwd"] = {"entry": "attn_fwd_ws (v_prep_kernel + attn_fwd_kernel per call)",
-                           "launches_per_step": launches["attn_fwd"], "avg_ms": round(attn_launch_ms, 4),
+    kernels["attn_fwd"] = {"entry": entry,
+                           "launches_per_step": n_attn, "avg_ms": round(attn_launch_ms, 4),
                            "flop_per_step": attn_flops, "tflops": round(attn_tflops, 2),
                            "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}
     if "qk_norm_rope" in per_kernel:
@@ -266,7 +303,7 @@ def main():
                                  "frac_hbm_peak": round(merge_bytes / (mer_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
     value = attn_flops / (ms_per_step * 1e-3) / 1e12
-    flop_per_launch = attn_flops / launches["attn_fwd"]
+    flop_per_launch = attn_flops / n_attn
     roofline = {"kernel": "attn_fwd_ws call (V rewrite + attention kernel)",
                 "bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -274,7 +311,8 @@ def main():
 
     workload_name = {
         "wan": "Wan2.2-shaped attention step B1 H40 S75600 D128: QK RMSNorm+3D RoPE, ring-overlap "
-               "attention (local 1/4 + remote 3/4 of the keys), fp32 LSE merge",
+               "attention (local 1/4 + remote 3/4 of the keys" + (", on two streams" if args.ring_streams == 2
+                                                                  else "") + "), fp32 LSE merge",
         "qwen": "Qwen-Image joint attention B1 H24 S4312 D128: QK RMSNorm+RoPE, attention",
         "cosmos": "Cosmos-Predict video attention B2 H16 S12480 D128: QK RMSNorm+3D RoPE, attention",
         "sp": "Wan2.2 4-way SP share: Sq 18900 x Skv 75600 H40 D128 as 4 KV chunks + 3 fp32 merges",

@@ -13,8 +13,8 @@ import torch
 
 import oracle
 from oracle import compare
-from attention_qk_norm_rope_amd import (attn_fwd, attn_fwd_workspace_bytes, attn_fwd_ws, attn_merge, inputs,
-                                        qk_norm_rope)
+from attention_qk_norm_rope_amd import (attn_fwd, attn_fwd_ring_overlap, attn_fwd_workspace_bytes, attn_fwd_ws,
+                                        attn_merge, inputs, qk_norm_rope)
 from gpu_common import dev_bits, dev_f32, host_bits, host_f64, rows_of, say, workload
 
 pytestmark = pytest.mark.gpu
@@ -100,6 +100,33 @@ def test_wan_ring_overlap_step():
     attn_merge(oa, la, ob, lb)
     torch.cuda.synchronize()
     _check_attn(cfg, host_bits(dq), host_bits(dk), x["v"], oa, la, "ring-overlap step")
+
+
+@pytest.mark.parametrize("index", [2, 3])
+def test_ring_overlap_two_streams(index):
+    """Ring Attention Overlap on one GPU: the local quarter of the keys on a
+    side stream, concurrently with the remote three quarters on the current
+    stream, then the LSE merge.  Same bits as the one-stream order, and the
+    oracle's full attention on sampled rows."""
+    cfg = inputs.CONFIGS[index]
+    x = workload(index)
+    dq, dk, cos, sin = _prologue(cfg, x)
+    dv = dev_bits(x["v"])
+    c = cfg.S // 4
+    mk_ws = lambda n: torch.empty((attn_fwd_workspace_bytes(cfg.B, cfg.H, n, cfg.D),), dtype=torch.uint8,  # noqa: E731
+                                  device=dq.device)
+    ws_a, ws_b = mk_ws(c), mk_ws(cfg.S - c)
+    say(f"[config {index}] ring overlap, one stream")
+    o1, l1 = attn_fwd_ring_overlap(dq, dk, dv, c, ws_a, ws_b, scale=cfg.scale)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dq.device)
+    say(f"[config {index}] ring overlap, two streams")
+    o2, l2 = attn_fwd_ring_overlap(dq, dk, dv, c, ws_a, ws_b, scale=cfg.scale, side_stream=side)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    _check_attn(cfg, host_bits(dq), host_bits(dk), x["v"], o2, l2, "ring overlap, two streams")
+    with pytest.raises(ValueError):
+        attn_fwd_ring_overlap(dq, dk, dv, c, ws_a, ws_a, scale=cfg.scale, side_stream=side)
 
 
 def test_sp_share_chains():
