@@ -46,10 +46,11 @@ def _load():
     lib.attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_kv_strided.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_ws.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_fwd_gqa.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_fwd_workspace_bytes.restype = i64
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
-    for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_merge"):
+    for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_merge"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -148,7 +149,7 @@ def _kv_bh_stride(t, B, H, S, D) -> int | None:
     return s1
 
 
-def _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse):
+def _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse, kv_heads=None):
     _need(q, "q", torch.bfloat16, q.device)
     dev = q.device
     _need(k, "k", torch.bfloat16, dev)
@@ -157,10 +158,11 @@ def _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse):
         raise ValueError("q, k, v must be 4-D BNSD")
     B, H, Sq, D = q.shape
     Skv = k.shape[2]
+    Hkv = H if kv_heads is None else kv_heads
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
-    sk = _kv_bh_stride(k, B, H, Skv, D)
-    sv = _kv_bh_stride(v, B, H, Skv, D)
+    sk = _kv_bh_stride(k, B, Hkv, Skv, D)
+    sv = _kv_bh_stride(v, B, Hkv, Skv, D)
     if sk is None or sv is None or sk != sv:
         raise ValueError("k and v must be [B,H,Skv,D] with contiguous rows and the same (b,h) stride")
     if scale is None:
@@ -225,6 +227,29 @@ def attn_fwd_ws(q, k, v, workspace, out=None, lse=None, scale: float | None = No
                              _ptr(lse), B, H, Sq, Skv, D, scale, 1 if causal else 0, _dtype_code(out),
                              _stream())
     _check("attn_fwd_ws", st)
+    return out, lse
+
+
+def attn_fwd_gqa(q, k, v, workspace=None, out=None, lse=None, scale: float | None = None,
+                 causal: bool = False, out_dtype=torch.bfloat16, return_lse: bool = True):
+    """Grouped-query attention: q bf16 [B,H,Sq,D]; k, v bf16 [B,Hkv,Skv,D]
+    (contiguous or key windows), H a multiple of Hkv; query head h reads K/V
+    head h // (H // Hkv).  With a workspace (at least
+    attn_fwd_workspace_bytes(B, Hkv, Skv, D) bytes) the workspace path runs.
+    Returns (out, lse)."""
+    if k.dim() != 4:
+        raise ValueError("k must be 4-D [B,Hkv,Skv,D]")
+    Hkv = k.shape[1]
+    (B, H, Sq, Skv, D), sk, scale, out, lse = _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse,
+                                                         kv_heads=Hkv)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = _load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), sk, ws_ptr, ws_bytes, _ptr(out), _ptr(lse), B, H, Hkv,
+                              Sq, Skv, D, scale, 1 if causal else 0, _dtype_code(out), _stream())
+    _check("attn_fwd_gqa", st)
     return out, lse
 
 

@@ -127,6 +127,12 @@ __device__ __forceinline__ int kswz(int key) {
     return D == 128 ? (key & 15) : ((key >> 1) & 7);
 }
 
+// K/V head of query head bh = b*H + h when G query heads share one K/V head
+// (grouped-query attention; G = 1 is plain multi-head attention).
+__device__ __forceinline__ int kv_head(int bh, int H, int G) {
+    return G == 1 ? bh : (bh / H) * (H / G) + (bh % H) / G;
+}
+
 // Workgroup id -> logical tile id, so that each XCD owns a contiguous range.
 __device__ __forceinline__ int xcd_remap(int wid, int nblk) {
     const int per = nblk >> 3, rem = nblk & 7, xcd = wid & 7;
@@ -211,7 +217,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, int64_t kv_bh_stride, void* __restrict__ out,
                 float* __restrict__ lse, int Sq, int Skv, float c, unsigned qsign, int causal,
-                int n_qtiles) {
+                int n_qtiles, int H, int G) {
     constexpr int BM = GEN_WAVES * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int KDMA = BN * D * 2 / 1024 / GEN_WAVES;  // 1 KB DMA chunks per wave per tile
@@ -228,6 +234,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = logical / n_qtiles;
+    const int bkv = kv_head(bh, H, G);
     int qt = logical - bh * n_qtiles;
     if (causal) qt = n_qtiles - 1 - qt;   // longest rows first
     const int q0 = qt * BM;
@@ -240,9 +247,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(q + (int64_t)bh * Sq * D), (short)0, Sq * D * 2, RSRC_WORD3);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(k + (int64_t)bh * kv_bh_stride), (short)0, Skv * D * 2, RSRC_WORD3);
+        (void*)(k + (int64_t)bkv * kv_bh_stride), (short)0, Skv * D * 2, RSRC_WORD3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(v + (int64_t)bh * kv_bh_stride), (short)0, Skv * D * 2, RSRC_WORD3);
+        (void*)(v + (int64_t)bkv * kv_bh_stride), (short)0, Skv * D * 2, RSRC_WORD3);
 
     // Q^T fragments: lane holds query (q0w + n), d = 16t + 8hh .. +7.
     bf16x8 qf[DT];
@@ -426,7 +433,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
                    float* __restrict__ lse, int Sq, int Skv, float c, unsigned qsign, int causal,
-                   int n_qtiles) {
+                   int n_qtiles, int H, int G) {
     constexpr int BM = WS_WAVES * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int TILE = BN * D;                         // elements of one K or V tile
@@ -442,6 +449,7 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = logical / n_qtiles;
+    const int bkv = kv_head(bh, H, G);
     int qt = logical - bh * n_qtiles;
     if (causal) qt = n_qtiles - 1 - qt;
     const int q0 = qt * BM;
@@ -471,7 +479,7 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // DMA sources: a buffer resource per tile, based at the tile (scalar
     // arithmetic), so every lane's offset is loop-invariant; the resource
     // ends at the last key of this head, and reads past it return zeros.
-    const uint16_t* kbh = k + (int64_t)bh * kv_bh_stride;
+    const uint16_t* kbh = k + (int64_t)bkv * kv_bh_stride;
     auto dma_k = [&](int kv0, auto b) {
         const int left = Skv - kv0;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -486,7 +494,7 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
     };
     // V tile `tile` of this head is the image at vbh + tile*TILE (tile < n_vt).
-    const uint16_t* vbh = vws + (int64_t)bh * n_vt * TILE;
+    const uint16_t* vbh = vws + (int64_t)bkv * n_vt * TILE;
     auto dma_v = [&](int tile, auto b) {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(vbh + (int64_t)tile * TILE), (short)0, TILE * 2, RSRC_WORD3);
@@ -649,7 +657,7 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
 template <int D, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
-                  int BH, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
+                  int BH, int H, int G, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
                   hipStream_t stream) {
     const int waves = vws ? WS_WAVES : GEN_WAVES;
     const int BM = waves * QPW;
@@ -659,18 +667,18 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
     if (vws)
         hipLaunchKernelGGL((attn_fwd_ws_kernel<D, OUT_F32>), dim3((unsigned)nblk), dim3(WS_WAVES * 64), 0, stream,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vws, kv_bh_stride, out, lse,
-                           Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles);
+                           Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G);
     else
         hipLaunchKernelGGL((attn_fwd_kernel<D, OUT_F32>), dim3((unsigned)nblk), dim3(GEN_WAVES * 64), 0, stream,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, kv_bh_stride, out, lse,
-                           Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles);
+                           Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
-                           void* out, float* lse, int BH, int Sq, int Skv, int D, float scale,
+                           void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
                            bool causal, bool out_f32, const void* vws, hipStream_t stream) {
     // Positive multiplier for exp2; the sign of the scale goes into Q.  A
     // zero (or vanishing) scale keeps a tiny positive multiplier so that
@@ -680,10 +688,10 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
     if (!(c >= 1e-30f)) c = 1e-30f;
     const unsigned qsign = scale < 0.f ? 0x80008000u : 0u;
     if (D == 128)
-        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, vws, stream)
-                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, vws, stream);
-    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, vws, stream)
-                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, Sq, Skv, c, qsign, causal, vws, stream);
+        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, stream)
+                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, stream);
+    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, stream)
+                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, stream);
 }
 
 }  // namespace dit

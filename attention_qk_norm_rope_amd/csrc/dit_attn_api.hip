@@ -69,9 +69,10 @@ struct AttnRanges {
 };
 
 int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
-               int B, int H, int Sq, int Skv, int D, float scale, int out_dtype, AttnRanges* r) {
+               int B, int H, int Hkv, int Sq, int Skv, int D, float scale, int out_dtype, AttnRanges* r) {
     if (!q || !k || !v || !out) return DIT_ERR_NULL;
     if (B < 1 || H < 1 || Sq < 1 || Skv < 1 || D < 1) return DIT_ERR_SHAPE;
+    if (Hkv < 1 || Hkv > H || H % Hkv != 0) return DIT_ERR_SHAPE;
     if (!isfinite(scale)) return DIT_ERR_SHAPE;
     if (D != 64 && D != 128) return DIT_ERR_UNSUPPORTED;
     if (out_dtype != DIT_BF16 && out_dtype != DIT_FP32) return DIT_ERR_UNSUPPORTED;
@@ -83,11 +84,12 @@ int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride
     if ((int64_t)(Sq + 512) * D * 2 > 0x7FFFFFFF || (int64_t)(Skv + 512) * D * 2 > 0x7FFFFFFF)
         return DIT_ERR_SHAPE;
     if (kv_bh_stride < (int64_t)Skv * D) return DIT_ERR_SHAPE;
-    if (kv_bh_stride > kMaxElems || (BH - 1) * kv_bh_stride > kMaxElems) return DIT_ERR_SHAPE;
+    const int64_t BHkv = (int64_t)B * Hkv;
+    if (kv_bh_stride > kMaxElems || (BHkv - 1) * kv_bh_stride > kMaxElems) return DIT_ERR_SHAPE;
     if (kv_bh_stride % 8 != 0) return DIT_ERR_ALIGN;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
         return DIT_ERR_ALIGN;
-    const int64_t kv_elems = (BH - 1) * kv_bh_stride + (int64_t)Skv * D;
+    const int64_t kv_elems = (BHkv - 1) * kv_bh_stride + (int64_t)Skv * D;
     r->q = range_of(q, q_elems * 2);
     r->k = range_of(k, kv_elems * 2);
     r->v = range_of(v, kv_elems * 2);
@@ -107,11 +109,8 @@ int attn_fwd_kv_strided(const void* q, const void* k, const void* v, int64_t kv_
                         float* lse, int B, int H, int Sq, int Skv, int D, float scale, int causal,
                         int out_dtype, hipStream_t stream) {
     AttnRanges r;
-    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Sq, Skv, D, scale, out_dtype, &r);
-    if (st != DIT_OK) return st;
-    (void)hipGetLastError();
-    return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, Sq, Skv, D, scale,
-                                           causal != 0, out_dtype == DIT_FP32, nullptr, stream));
+    return attn_fwd_gqa(q, k, v, kv_bh_stride, nullptr, 0, out, lse, B, H, H, Sq, Skv, D, scale, causal,
+                        out_dtype, stream);
 }
 
 int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D) {
@@ -124,21 +123,36 @@ int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D) {
 int attn_fwd_ws(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
                 int64_t workspace_bytes, void* out, float* lse, int B, int H, int Sq, int Skv, int D,
                 float scale, int causal, int out_dtype, hipStream_t stream) {
+    if (!workspace) {
+        AttnRanges r;
+        const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, H, Sq, Skv, D, scale, out_dtype, &r);
+        return st != DIT_OK ? st : DIT_ERR_NULL;
+    }
+    return attn_fwd_gqa(q, k, v, kv_bh_stride, workspace, workspace_bytes, out, lse, B, H, H, Sq, Skv, D, scale,
+                        causal, out_dtype, stream);
+}
+
+int attn_fwd_gqa(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
+                 int64_t workspace_bytes, void* out, float* lse, int B, int H, int Hkv, int Sq, int Skv, int D,
+                 float scale, int causal, int out_dtype, hipStream_t stream) {
     AttnRanges r;
-    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Sq, Skv, D, scale, out_dtype, &r);
+    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Hkv, Sq, Skv, D, scale, out_dtype, &r);
     if (st != DIT_OK) return st;
-    if (!workspace) return DIT_ERR_NULL;
-    if (!aligned(workspace, 16)) return DIT_ERR_ALIGN;
-    const int64_t need = attn_fwd_workspace_bytes(B, H, Skv, D);
-    if (need < 0 || workspace_bytes < need) return DIT_ERR_SHAPE;
-    const Range rw = range_of(workspace, need);
-    if (overlap(rw, r.q) || overlap(rw, r.k) || overlap(rw, r.v) || overlap(rw, r.out) ||
-        (lse && overlap(rw, r.lse)))
-        return DIT_ERR_ALIAS;
+    if (workspace) {
+        if (!aligned(workspace, 16)) return DIT_ERR_ALIGN;
+        const int64_t need = attn_fwd_workspace_bytes(B, Hkv, Skv, D);
+        if (need < 0 || workspace_bytes < need) return DIT_ERR_SHAPE;
+        const Range rw = range_of(workspace, need);
+        if (overlap(rw, r.q) || overlap(rw, r.k) || overlap(rw, r.v) || overlap(rw, r.out) ||
+            (lse && overlap(rw, r.lse)))
+            return DIT_ERR_ALIAS;
+    }
     (void)hipGetLastError();
-    hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * H, Skv, D, stream);
-    if (e != hipSuccess) return DIT_ERR_HIP;
-    return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, Sq, Skv, D, scale,
+    if (workspace) {
+        const hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * Hkv, Skv, D, stream);
+        if (e != hipSuccess) return DIT_ERR_HIP;
+    }
+    return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, H, H / Hkv, Sq, Skv, D, scale,
                                            causal != 0, out_dtype == DIT_FP32, workspace, stream));
 }
 

@@ -7,10 +7,12 @@
 
 namespace dit {
 
-// Attention: q [BH,Sq,D] bf16; k/v rows at k + bh*kv_bh_stride + j*D.  With
-// vws != null, V is read from the prepared tiles written by launch_v_prep.
+// Attention: q [BH,Sq,D] bf16 with BH = B*H query heads; query head
+// bh = b*H + h reads K/V head g = b*(H/G) + h/G, rows at k + g*kv_bh_stride
+// + j*D (G = 1: g = bh).  With vws != null, V is read from the prepared tiles
+// written by launch_v_prep over the B*H/G K/V heads.
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
-                           void* out, float* lse, int BH, int Sq, int Skv, int D, float scale,
+                           void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
                            bool causal, bool out_f32, const void* vws, hipStream_t stream);
 
 // Bytes of prepared V for BH heads of Skv keys; launch_v_prep writes them.

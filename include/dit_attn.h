@@ -4,6 +4,7 @@
  *
  *   qk_norm_rope   per-head RMSNorm of q and k, then interleaved rotary, in place
  *   attn_fwd       softmax(scale * Q K^T) V with a per-row log-sum-exp (BNSD)
+ *   attn_fwd_gqa   the same with Hkv K/V heads shared by H query heads
  *   attn_merge     fold of two partial attentions over disjoint key sets
  *
  * Sources of the operations (page title, section):
@@ -139,6 +140,28 @@ int attn_fwd_ws(const void *q, const void *k, const void *v, int64_t kv_bh_strid
 /* Workspace bytes attn_fwd_ws needs (B*H * ceil(Skv/64) * 64 * D * 2), or -1
  * for arguments attn_fwd_ws would reject. */
 int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D);
+
+/*
+ * Grouped-query attention: [WAN] npu_fused_infer_attention_score takes a
+ * num_key_value_heads argument, so Hkv K/V heads serve H query heads.
+ *
+ * Query head (b,h) attends to K/V head (b, h / (H/Hkv)). That K/V head is read
+ * at k + (b*Hkv + h/(H/Hkv)) * kv_bh_stride + j*D (same for v). H must be a
+ * multiple of Hkv, and Hkv = H is plain multi-head attention. q, out and lse
+ * are [B,H,...] as in attn_fwd; k and v hold B*Hkv heads.
+ *
+ * The workspace is optional:
+ *   - NULL: runs the path of attn_fwd_kv_strided.
+ *   - non-NULL: runs the path of attn_fwd_ws. It needs at least
+ *     attn_fwd_workspace_bytes(B, Hkv, Skv, D) bytes; V is rewritten once per
+ *     K/V head.
+ * Both paths give identical bits. Other arguments, results and errors are as
+ * for attn_fwd_ws. DIT_ERR_SHAPE when Hkv < 1 or H % Hkv != 0.
+ */
+int attn_fwd_gqa(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
+                 void *workspace, int64_t workspace_bytes, void *out, float *lse,
+                 int B, int H, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                 int out_dtype, hipStream_t stream);
 
 /*
  * Merge of two partial attentions over disjoint key sets, in place into

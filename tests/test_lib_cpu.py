@@ -44,6 +44,7 @@ def lib():
     lib.attn_fwd_ws.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_fwd_workspace_bytes.restype = i64
+    lib.attn_fwd_gqa.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
     lib.dit_attn_version.restype = ctypes.c_char_p
@@ -53,7 +54,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
-                          "attn_fwd_workspace_bytes", "attn_merge", "dit_attn_status_string",
+                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_merge", "dit_attn_status_string",
                           "dit_attn_version"}, names
     for name in names:
         assert hasattr(lib, name), name
@@ -134,6 +135,23 @@ def test_attn_fwd_ws_rejections(lib):
     assert call(ws=L) == ALIAS                           # workspace on lse
     assert call(o=None) == NULL                          # the attention checks come first
     assert call(stride=255 * 64) == SHAPE
+
+
+def test_attn_fwd_gqa_rejections(lib):
+    f = lib.attn_fwd_gqa
+    # B1, H4 query heads over Hkv K/V heads of Skv 256, D64.
+    def call(Hkv=2, ws=None, nbytes=0, stride=256 * 64, o=O):
+        return f(Q, K, V, stride, ws, nbytes, o, L, 1, 4, Hkv, 256, 256, 64, 0.125, 0, BF16, None)
+
+    assert call(Hkv=0) == SHAPE
+    assert call(Hkv=3) == SHAPE                          # 4 % 3 != 0
+    assert call(Hkv=8) == SHAPE                          # more K/V heads than query heads
+    assert call(o=None) == NULL
+    assert call(stride=255 * 64) == SHAPE
+    need = 2 * 4 * 64 * 64 * 2                           # B*Hkv * 4 tiles * 64 keys * D * 2 B
+    assert call(ws=WS, nbytes=need - 1) == SHAPE         # sized by Hkv, not H
+    assert call(ws=WS + 8, nbytes=need) == ALIGN
+    assert call(ws=Q + 4096, nbytes=need) == ALIAS
 
 
 def test_qk_norm_rope_rejections(lib):
