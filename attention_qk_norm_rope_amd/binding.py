@@ -49,8 +49,11 @@ def _load():
     lib.attn_fwd_gqa.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_fwd_workspace_bytes.restype = i64
+    lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
+                                        i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
-    for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_merge"):
+    for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_fwd_ws_fused_q",
+                 "attn_merge"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -250,6 +253,31 @@ def attn_fwd_gqa(q, k, v, workspace=None, out=None, lse=None, scale: float | Non
     st = _load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), sk, ws_ptr, ws_bytes, _ptr(out), _ptr(lse), B, H, Hkv,
                               Sq, Skv, D, scale, 1 if causal else 0, _dtype_code(out), _stream())
     _check("attn_fwd_gqa", st)
+    return out, lse
+
+
+def attn_fwd_ws_fused_q(q, k, v, workspace, w_q, cos_q, sin_q, eps: float, out=None, lse=None,
+                        scale: float | None = None, causal: bool = False, out_dtype=torch.bfloat16,
+                        return_lse: bool = True):
+    """attn_fwd_ws with the query RMSNorm + rotary fused into the Q load: q
+    holds raw rows (read only); w_q fp32 [D]; cos_q, sin_q fp32 [Sq, D].  k
+    must already be normalised and rotated.  Same bits as
+    qk_norm_rope(q, None, w_q, None, cos_q, sin_q, eps) then attn_fwd_ws."""
+    (B, H, Sq, Skv, D), sk, scale, out, lse = _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    _need(w_q, "w_q", torch.float32, q.device)
+    if tuple(w_q.shape) != (D,) or not w_q.is_contiguous():
+        raise ValueError(f"w_q must be contiguous [{D}]")
+    for t, name in ((cos_q, "cos_q"), (sin_q, "sin_q")):
+        _need(t, name, torch.float32, q.device)
+        if tuple(t.shape) != (Sq, D) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [{Sq},{D}]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _load().attn_fwd_ws_fused_q(_ptr(q), _ptr(k), _ptr(v), sk, _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                                     _ptr(w_q), _ptr(cos_q), _ptr(sin_q), float(eps), B, H, Sq, Skv, D, scale,
+                                     1 if causal else 0, _dtype_code(out), _stream())
+    _check("attn_fwd_ws_fused_q", st)
     return out, lse
 
 

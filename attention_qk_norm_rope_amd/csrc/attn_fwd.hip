@@ -51,6 +51,7 @@
 //    over 8 XCDs) works on a contiguous range of (b,h, q-tile): the query
 //    tiles of one head share that head's K/V through one XCD's L2.
 #include "internal.h"
+#include "norm_rope.h"
 
 #include <math.h>
 
@@ -427,13 +428,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // slice of the softmax and the LDS fragment reads of the next chunk.  The
 // lazy O rescale of tile j is applied after P_{j-1} V_{j-1}.  One barrier
 // per tile; during sub-iteration j the DMAs of K_{j+2} and V_j are in flight.
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool FQ>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WS_WAVES * 64, WS_WAVES * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
                    float* __restrict__ lse, int Sq, int Skv, float c, unsigned qsign, int causal,
-                   int n_qtiles, int H, int G) {
+                   int n_qtiles, int H, int G, QNormRope qn) {
     constexpr int BM = WS_WAVES * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int TILE = BN * D;                         // elements of one K or V tile
@@ -463,11 +464,69 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(q + (int64_t)bh * Sq * D), (short)0, Sq * D * 2, RSRC_WORD3);
     bf16x8 qf[DT];
+    if constexpr (!FQ) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, ((q0w + n) * D + 16 * t + 8 * hh) * 2, 0, 0);
-        x ^= qsign;
-        qf[t] = __builtin_bit_cast(bf16x8, x);
+        for (int t = 0; t < DT; ++t) {
+            u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, ((q0w + n) * D + 16 * t + 8 * hh) * 2, 0, 0);
+            x ^= qsign;
+            qf[t] = __builtin_bit_cast(bf16x8, x);
+        }
+    } else {
+        // RMSNorm + rotary of the raw query row, as qk_norm_rope computes it:
+        // the lane holds the 16-byte chunks ch = 2t + hh of its row, so the
+        // xor tree of chunk sums (partners D/16 chunks apart first) is a tree
+        // over t followed by the cross-half pair.
+        const int qi = q0w + n;
+        unsigned raw[DT][4];
+        float cs[DT];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * D + 16 * t + 8 * hh) * 2, 0, 0);
+            float xv[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) raw[t][i] = x[i];
+            nr::unpack8(raw[t], xv);
+            cs[t] = nr::chunk_sumsq(xv);
+        }
+#pragma unroll
+        for (int m = DT / 2; m >= 1; m >>= 1)
+#pragma unroll
+            for (int t = 0; t < m; ++t) cs[t] += cs[t + m];
+        const float total = pair_sum(cs[0]);
+        const float inv_r = qi < Sq ? nr::rms_inv(total, 1.0f / (float)D, qn.eps) : 0.f;
+        // Tables [Sq, D]: rows past Sq read as zeros.
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void*)qn.cos_t, (short)0, Sq * D * 4,
+                                                                            RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)qn.sin_t, (short)0, Sq * D * 4,
+                                                                            RSRC_WORD3);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const int d0 = 16 * t + 8 * hh;
+            const f32x4 w0 = *(const f32x4*)(qn.w + d0), w1 = *(const f32x4*)(qn.w + d0 + 4);
+            // Whole-vector bit casts: a bit cast of one element of a vector
+            // (an lvalue) is lowered as element 0 by this compiler.
+            const f32x4 c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (qi * D + d0) * 4, 0, 0));
+            const f32x4 c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (qi * D + d0 + 4) * 4, 0, 0));
+            const f32x4 s0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (qi * D + d0) * 4, 0, 0));
+            const f32x4 s1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (qi * D + d0 + 4) * 4, 0, 0));
+            const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+            float cv[8], sv[8], xv[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cv[i] = c0[i];
+                cv[i + 4] = c1[i];
+                sv[i] = s0[i];
+                sv[i + 4] = s1[i];
+            }
+            nr::unpack8(raw[t], xv);
+            u32x4 r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                r[i] = nr::pair(xv[2 * i], xv[2 * i + 1], inv_r, wv[2 * i], wv[2 * i + 1], cv[2 * i], cv[2 * i + 1],
+                                sv[2 * i], sv[2 * i + 1]);
+            r ^= qsign;
+            qf[t] = __builtin_bit_cast(bf16x8, r);
+        }
     }
 
     int n_tiles = n_vt;
@@ -658,16 +717,20 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 template <int D, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
                   int BH, int H, int G, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
-                  hipStream_t stream) {
+                  const QNormRope* qn, hipStream_t stream) {
     const int waves = vws ? WS_WAVES : GEN_WAVES;
     const int BM = waves * QPW;
     const int n_qtiles = (Sq + BM - 1) / BM;
     const int64_t nblk = (int64_t)n_qtiles * BH;
     if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (vws)
-        hipLaunchKernelGGL((attn_fwd_ws_kernel<D, OUT_F32>), dim3((unsigned)nblk), dim3(WS_WAVES * 64), 0, stream,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vws, kv_bh_stride, out, lse,
-                           Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G);
+    if (vws && qn)
+        hipLaunchKernelGGL((attn_fwd_ws_kernel<D, OUT_F32, true>), dim3((unsigned)nblk), dim3(WS_WAVES * 64), 0,
+                           stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vws, kv_bh_stride, out,
+                           lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, *qn);
+    else if (vws)
+        hipLaunchKernelGGL((attn_fwd_ws_kernel<D, OUT_F32, false>), dim3((unsigned)nblk), dim3(WS_WAVES * 64), 0,
+                           stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vws, kv_bh_stride, out,
+                           lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, QNormRope{});
     else
         hipLaunchKernelGGL((attn_fwd_kernel<D, OUT_F32>), dim3((unsigned)nblk), dim3(GEN_WAVES * 64), 0, stream,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, kv_bh_stride, out, lse,
@@ -679,7 +742,7 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
-                           bool causal, bool out_f32, const void* vws, hipStream_t stream) {
+                           bool causal, bool out_f32, const void* vws, const QNormRope* qn, hipStream_t stream) {
     // Positive multiplier for exp2; the sign of the scale goes into Q.  A
     // zero (or vanishing) scale keeps a tiny positive multiplier so that
     // masked logits (-inf) still map to probability 0; the logits it yields
@@ -688,10 +751,10 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
     if (!(c >= 1e-30f)) c = 1e-30f;
     const unsigned qsign = scale < 0.f ? 0x80008000u : 0u;
     if (D == 128)
-        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, stream)
-                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, stream);
-    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, stream)
-                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, stream);
+        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, stream)
+                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, stream);
+    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, stream)
+                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, stream);
 }
 
 }  // namespace dit

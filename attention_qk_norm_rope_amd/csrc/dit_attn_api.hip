@@ -101,6 +101,40 @@ int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride
     return DIT_OK;
 }
 
+// Attention launch shared by the entry points: optional workspace (V images),
+// optional fused Q prologue (workspace path only), Hkv K/V heads.
+int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
+                int64_t workspace_bytes, void* out, float* lse, int B, int H, int Hkv, int Sq, int Skv, int D,
+                float scale, int causal, int out_dtype, const dit::QNormRope* qn, hipStream_t stream) {
+    AttnRanges r;
+    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Hkv, Sq, Skv, D, scale, out_dtype, &r);
+    if (st != DIT_OK) return st;
+    if (workspace) {
+        if (!aligned(workspace, 16)) return DIT_ERR_ALIGN;
+        const int64_t need = attn_fwd_workspace_bytes(B, Hkv, Skv, D);
+        if (need < 0 || workspace_bytes < need) return DIT_ERR_SHAPE;
+        const Range rw = range_of(workspace, need);
+        if (overlap(rw, r.q) || overlap(rw, r.k) || overlap(rw, r.v) || overlap(rw, r.out) ||
+            (lse && overlap(rw, r.lse)))
+            return DIT_ERR_ALIAS;
+        if (qn) {
+            if (!aligned(qn->w, 16) || !aligned(qn->cos_t, 16) || !aligned(qn->sin_t, 16)) return DIT_ERR_ALIGN;
+            const int64_t tbytes = (int64_t)Sq * D * 4;
+            const Range rt[3] = {range_of(qn->w, (int64_t)D * 4), range_of(qn->cos_t, tbytes),
+                                 range_of(qn->sin_t, tbytes)};
+            for (const Range& t : rt)
+                if (overlap(t, r.out) || overlap(t, rw) || (lse && overlap(t, r.lse))) return DIT_ERR_ALIAS;
+        }
+    }
+    (void)hipGetLastError();
+    if (workspace) {
+        const hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * Hkv, Skv, D, stream);
+        if (e != hipSuccess) return DIT_ERR_HIP;
+    }
+    return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, H, H / Hkv, Sq, Skv, D, scale,
+                                           causal != 0, out_dtype == DIT_FP32, workspace, qn, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,7 +142,6 @@ extern "C" {
 int attn_fwd_kv_strided(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out,
                         float* lse, int B, int H, int Sq, int Skv, int D, float scale, int causal,
                         int out_dtype, hipStream_t stream) {
-    AttnRanges r;
     return attn_fwd_gqa(q, k, v, kv_bh_stride, nullptr, 0, out, lse, B, H, H, Sq, Skv, D, scale, causal,
                         out_dtype, stream);
 }
@@ -135,25 +168,25 @@ int attn_fwd_ws(const void* q, const void* k, const void* v, int64_t kv_bh_strid
 int attn_fwd_gqa(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
                  int64_t workspace_bytes, void* out, float* lse, int B, int H, int Hkv, int Sq, int Skv, int D,
                  float scale, int causal, int out_dtype, hipStream_t stream) {
-    AttnRanges r;
-    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Hkv, Sq, Skv, D, scale, out_dtype, &r);
-    if (st != DIT_OK) return st;
-    if (workspace) {
-        if (!aligned(workspace, 16)) return DIT_ERR_ALIGN;
-        const int64_t need = attn_fwd_workspace_bytes(B, Hkv, Skv, D);
-        if (need < 0 || workspace_bytes < need) return DIT_ERR_SHAPE;
-        const Range rw = range_of(workspace, need);
-        if (overlap(rw, r.q) || overlap(rw, r.k) || overlap(rw, r.v) || overlap(rw, r.out) ||
-            (lse && overlap(rw, r.lse)))
-            return DIT_ERR_ALIAS;
+    return attn_common(q, k, v, kv_bh_stride, workspace, workspace_bytes, out, lse, B, H, Hkv, Sq, Skv, D, scale,
+                       causal, out_dtype, nullptr, stream);
+}
+
+int attn_fwd_ws_fused_q(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
+                        int64_t workspace_bytes, void* out, float* lse, const float* w_q, const float* cos_q,
+                        const float* sin_q, float eps, int B, int H, int Sq, int Skv, int D, float scale,
+                        int causal, int out_dtype, hipStream_t stream) {
+    if (!workspace || !w_q || !cos_q || !sin_q) {
+        AttnRanges r;
+        const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, H, Sq, Skv, D, scale, out_dtype, &r);
+        return st != DIT_OK ? st : DIT_ERR_NULL;
     }
-    (void)hipGetLastError();
-    if (workspace) {
-        const hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * Hkv, Skv, D, stream);
-        if (e != hipSuccess) return DIT_ERR_HIP;
-    }
-    return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, H, H / Hkv, Sq, Skv, D, scale,
-                                           causal != 0, out_dtype == DIT_FP32, workspace, stream));
+    if (!(eps >= 0.f) || !isfinite(eps)) return DIT_ERR_SHAPE;
+    // The kernel reads the tables with 32-bit buffer offsets.
+    if ((int64_t)Sq * D * 4 > 0x7FFFFFFF) return DIT_ERR_SHAPE;
+    const dit::QNormRope qn{w_q, cos_q, sin_q, eps};
+    return attn_common(q, k, v, kv_bh_stride, workspace, workspace_bytes, out, lse, B, H, H, Sq, Skv, D, scale,
+                       causal, out_dtype, &qn, stream);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Sq,

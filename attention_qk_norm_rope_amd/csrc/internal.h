@@ -11,9 +11,18 @@ namespace dit {
 // bh = b*H + h reads K/V head g = b*(H/G) + h/G, rows at k + g*kv_bh_stride
 // + j*D (G = 1: g = bh).  With vws != null, V is read from the prepared tiles
 // written by launch_v_prep over the B*H/G K/V heads.
+// With qn != null (workspace path only), q holds the raw rows and the kernel
+// applies the per-head RMSNorm + interleaved rotary of qk_norm_rope to them
+// as it loads them (same bits as running qk_norm_rope on q first).
+struct QNormRope {
+    const float* w;      // [D]
+    const float* cos_t;  // [Sq, D]
+    const float* sin_t;  // [Sq, D]
+    float eps;
+};
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
-                           bool causal, bool out_f32, const void* vws, hipStream_t stream);
+                           bool causal, bool out_f32, const void* vws, const QNormRope* qn, hipStream_t stream);
 
 // Bytes of prepared V for BH heads of Skv keys; launch_v_prep writes them.
 int64_t v_prep_bytes(int64_t BH, int Skv, int D);

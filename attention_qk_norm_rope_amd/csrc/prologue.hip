@@ -12,6 +12,7 @@
 // wave streams 4 (D=128) or 8 (D=64) rows of 256/128 contiguous bytes.  The
 // sum of squares is reduced across those lanes with xor shuffles.
 #include "internal.h"
+#include "norm_rope.h"
 
 namespace dit {
 namespace {
@@ -21,10 +22,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-    f32x2 f = {a, b};
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
-}
 
 // Grid: x = blocks of RPB sequence positions, y = q or k, z = groups of HB
 // heads.  A thread loads the cos/sin/weight values of its row slice once and
@@ -79,26 +76,18 @@ qk_norm_rope_kernel(uint16_t* __restrict__ q, uint16_t* __restrict__ k, const fl
         for (int u = 0; u < UNR; ++u) {
             if (bh + u >= bh1) break;
             float xv[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xv[2 * i] = __builtin_bit_cast(float, raw[u][i] << 16);
-                xv[2 * i + 1] = __builtin_bit_cast(float, raw[u][i] & 0xFFFF0000u);
-            }
-            float ss = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(xv[i], xv[i], ss);
+            const unsigned rw[4] = {raw[u][0], raw[u][1], raw[u][2], raw[u][3]};
+            nr::unpack8(rw, xv);
+            // Chunk sums combined as an xor tree over the L lanes of the row.
+            float ss = nr::chunk_sumsq(xv);
 #pragma unroll
             for (int m = L / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-            const float inv_r = 1.0f / sqrtf(ss * inv_d + eps);
+            const float inv_r = nr::rms_inv(ss, inv_d, eps);
             u32x4 res;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ya = xv[2 * i] * inv_r * wv[2 * i];
-                const float yb = xv[2 * i + 1] * inv_r * wv[2 * i + 1];
-                const float za = ya * cv[2 * i] - yb * sv[2 * i];
-                const float zb = yb * cv[2 * i + 1] + ya * sv[2 * i + 1];
-                res[i] = pack_bf16(za, zb);
-            }
+            for (int i = 0; i < 4; ++i)
+                res[i] = nr::pair(xv[2 * i], xv[2 * i + 1], inv_r, wv[2 * i], wv[2 * i + 1], cv[2 * i],
+                                  cv[2 * i + 1], sv[2 * i], sv[2 * i + 1]);
             *(u32x4*)(x + ((int64_t)(bh + u) * S + s) * D + d0) = res;
         }
     }

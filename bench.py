@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan", choices=["wan", "qwen", "cosmos", "sp"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fuse-q", action="store_true",
+                    help="wan workload: apply the query RMSNorm+RoPE inside the attention's Q load "
+                         "(attn_fwd_ws_fused_q); the prologue kernel then normalises k only")
     ap.add_argument("--ring-streams", type=int, default=1, choices=[1, 2],
                     help="wan workload: run the local and remote attention calls on one stream in order (1) "
                          "or concurrently on two streams (2)")
@@ -112,8 +115,8 @@ def main():
     import numpy as np
     import torch
 
-    from attention_qk_norm_rope_amd import (attn_fwd_ring_overlap, attn_fwd_workspace_bytes, attn_fwd_ws, attn_merge,
-                                            inputs, qk_norm_rope)
+    from attention_qk_norm_rope_amd import (attn_fwd_ring_overlap, attn_fwd_workspace_bytes, attn_fwd_ws,
+                                            attn_fwd_ws_fused_q, attn_merge, inputs, qk_norm_rope)
     from attention_qk_norm_rope_amd import binding
 
     if not torch.cuda.is_available():
@@ -178,6 +181,32 @@ def main():
 
         final_out, final_lse = out_a, lse_a
         n_merge = 0
+    elif wl == "wan" and args.fuse_q:
+        c = S // 4
+        out_a = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+        out_b = torch.empty_like(out_a)
+        lse_a = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+        lse_b = torch.empty_like(lse_a)
+        names = ["qk_norm_rope", "attn_fwd", "attn_fwd", "attn_merge"]
+
+        def step(ev):
+            k.copy_(k0)
+            ev[0].record()
+            qk_norm_rope(None, k, None, w_k, cos_d, sin_d, cfg.eps)
+            ev[1].record()
+            attn_fwd_ws_fused_q(q0, k[:, :, :c], v[:, :, :c], ws, w_q, cos_d, sin_d, cfg.eps, out=out_a, lse=lse_a,
+                                scale=scale)
+            ev[2].record()
+            attn_fwd_ws_fused_q(q0, k[:, :, c:], v[:, :, c:], ws, w_q, cos_d, sin_d, cfg.eps, out=out_b, lse=lse_b,
+                                scale=scale)
+            ev[3].record()
+            attn_merge(out_a, lse_a, out_b, lse_b)
+            ev[4].record()
+
+        final_out, final_lse = out_a, lse_a
+        merge_rows = B * H * Sq
+        merge_bytes = merge_rows * (D * (4 + 4 + 4) + 12)
+        n_merge = 1
     elif wl == "wan":
         c = S // 4
         out_a = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
@@ -292,7 +321,7 @@ def main():
                            "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}
     if "qk_norm_rope" in per_kernel:
         pro_ms = sum(per_kernel["qk_norm_rope"]) / args.steps
-        pro_bytes = 2 * (2 + 2) * B * H * S * D + 2 * S * D * 4
+        pro_bytes = (1 if args.fuse_q else 2) * (2 + 2) * B * H * S * D + 2 * S * D * 4
         kernels["qk_norm_rope"] = {"avg_ms": round(pro_ms, 4), "bytes": pro_bytes,
                                    "gbs": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
                                    "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -312,7 +341,8 @@ def main():
     workload_name = {
         "wan": "Wan2.2-shaped attention step B1 H40 S75600 D128: QK RMSNorm+3D RoPE, ring-overlap "
                "attention (local 1/4 + remote 3/4 of the keys" + (", on two streams" if args.ring_streams == 2
-                                                                  else "") + "), fp32 LSE merge",
+                                                                  else "") + "), fp32 LSE merge"
+               + ("; query RMSNorm+RoPE fused into the attention's Q load" if args.fuse_q else ""),
         "qwen": "Qwen-Image joint attention B1 H24 S4312 D128: QK RMSNorm+RoPE, attention",
         "cosmos": "Cosmos-Predict video attention B2 H16 S12480 D128: QK RMSNorm+3D RoPE, attention",
         "sp": "Wan2.2 4-way SP share: Sq 18900 x Skv 75600 H40 D128 as 4 KV chunks + 3 fp32 merges",
@@ -335,6 +365,12 @@ def main():
         if wl == "sp":
             q_bits, k_bits = x["q"], x["k"]
         else:
+            if args.fuse_q:
+                # The fused step never writes q: the attention saw the prologue
+                # of q0, which qk_norm_rope reproduces bit for bit.
+                q.copy_(q0)
+                qk_norm_rope(q, None, w_q, None, cos_d, sin_d, cfg.eps)
+                torch.cuda.synchronize()
             q_bits = q.cpu().view(torch.int16).numpy().view(np.uint16)
             k_bits = k.cpu().view(torch.int16).numpy().view(np.uint16)
         threads = oracle.default_threads()

@@ -5,6 +5,7 @@
  *   qk_norm_rope   per-head RMSNorm of q and k, then interleaved rotary, in place
  *   attn_fwd       softmax(scale * Q K^T) V with a per-row log-sum-exp (BNSD)
  *   attn_fwd_gqa   the same with Hkv K/V heads shared by H query heads
+ *   attn_fwd_ws_fused_q  attention with the query prologue fused into its Q load
  *   attn_merge     fold of two partial attentions over disjoint key sets
  *
  * Sources of the operations (page title, section):
@@ -162,6 +163,27 @@ int attn_fwd_gqa(const void *q, const void *k, const void *v, int64_t kv_bh_stri
                  void *workspace, int64_t workspace_bytes, void *out, float *lse,
                  int B, int H, int Hkv, int Sq, int Skv, int D, float scale, int causal,
                  int out_dtype, hipStream_t stream);
+
+/*
+ * attn_fwd_ws with the query half of qk_norm_rope fused into the attention's
+ * query load ([COSMOS] §3.2-§3.3, [WAN] rms_norm and rotary_mul sections).
+ * q holds the raw query rows and is only read. Each row is normalised over D,
+ * weighted by w_q and rotated with the tables at its own position i, exactly
+ * as qk_norm_rope computes it, then rounded to bf16. The results are the bits
+ * of qk_norm_rope(q, NULL, w_q, ...) followed by attn_fwd_ws. k must already
+ * hold normalised, rotated keys (e.g. qk_norm_rope with q = NULL).
+ *
+ *   w_q           fp32 [D], 16-byte aligned
+ *   cos_q, sin_q  fp32 [Sq, D], 16-byte aligned; row i belongs to query row i
+ *   eps           >= 0 and finite
+ * Neither the tables nor w_q may overlap out, lse or the workspace. All other
+ * arguments and errors are as for attn_fwd_ws.
+ */
+int attn_fwd_ws_fused_q(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
+                        void *workspace, int64_t workspace_bytes, void *out, float *lse,
+                        const float *w_q, const float *cos_q, const float *sin_q, float eps,
+                        int B, int H, int Sq, int Skv, int D, float scale, int causal,
+                        int out_dtype, hipStream_t stream);
 
 /*
  * Merge of two partial attentions over disjoint key sets, in place into

@@ -45,6 +45,8 @@ def lib():
     lib.attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_fwd_workspace_bytes.restype = i64
     lib.attn_fwd_gqa.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
+                                        i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
     lib.dit_attn_version.restype = ctypes.c_char_p
@@ -54,7 +56,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
-                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_merge", "dit_attn_status_string",
+                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_merge", "dit_attn_status_string",
                           "dit_attn_version"}, names
     for name in names:
         assert hasattr(lib, name), name
@@ -152,6 +154,30 @@ def test_attn_fwd_gqa_rejections(lib):
     assert call(ws=WS, nbytes=need - 1) == SHAPE         # sized by Hkv, not H
     assert call(ws=WS + 8, nbytes=need) == ALIGN
     assert call(ws=Q + 4096, nbytes=need) == ALIAS
+
+
+TAB = 0x20_0000_0000
+
+
+def test_attn_fwd_ws_fused_q_rejections(lib):
+    f = lib.attn_fwd_ws_fused_q
+    need = 2 * 4 * 64 * 64 * 2
+    tb = 256 * 64 * 4                                    # one [Sq, D] fp32 table
+
+    def call(ws=WS, w=TAB, cq=TAB + 4096, sq=TAB + 4096 + tb, eps=1e-6, o=O):
+        return f(Q, K, V, 256 * 64, ws, need, o, L, w, cq, sq, eps, 1, 2, 256, 256, 64, 0.125, 0, BF16, None)
+
+    assert call(ws=None) == NULL
+    assert call(w=None) == NULL
+    assert call(cq=None) == NULL
+    assert call(sq=None) == NULL
+    assert call(eps=-1.0) == SHAPE
+    assert call(eps=float("nan")) == SHAPE
+    assert call(w=TAB + 8) == ALIGN
+    assert call(cq=TAB + 4096 + 4) == ALIGN
+    assert call(cq=O) == ALIAS                           # a table on the output
+    assert call(sq=WS) == ALIAS                          # a table on the workspace
+    assert call(o=None) == NULL
 
 
 def test_qk_norm_rope_rejections(lib):
