@@ -52,8 +52,10 @@ def _load():
     lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
                                         i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
+    lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
+    lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_fwd_ws_fused_q",
-                 "attn_merge"):
+                 "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -338,3 +340,38 @@ def attn_fwd_ring_overlap(q, k, v, split: int, ws_local, ws_remote, out_local=No
         main.wait_stream(side_stream)
     attn_merge(out_local, lse_local, out_remote, lse_remote)
     return out_local, lse_local
+
+
+def _layout_check(x, name):
+    if not isinstance(x, torch.Tensor) or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 4-D tensor")
+    if x.element_size() != 2:
+        raise TypeError(f"{name} must have 2-byte elements (bf16)")
+
+
+def bsnd_to_bnsd(x, h0: int = 0, heads: int | None = None, out=None):
+    """Head slice [h0, h0+heads) of BSND x [B,S,H,D] as BNSD [B,heads,S,D]."""
+    _layout_check(x, "x")
+    B, S, H, D = x.shape
+    heads = H - h0 if heads is None else heads
+    if out is None:
+        out = torch.empty((B, heads, S, D), dtype=x.dtype, device=x.device)
+    _layout_check(out, "out")
+    if tuple(out.shape) != (B, heads, S, D) or out.device != x.device:
+        raise ValueError(f"out must be [{B},{heads},{S},{D}] on {x.device}")
+    st = _load().bsnd_to_bnsd(_ptr(x), _ptr(out), B, S, H, h0, heads, D, _stream())
+    _check("bsnd_to_bnsd", st)
+    return out
+
+
+def bnsd_to_bsnd(o, x, h0: int = 0):
+    """Write BNSD o [B,Hs,S,D] into the head slice [h0, h0+Hs) of BSND x
+    [B,S,H,D] (other heads untouched).  Returns x."""
+    _layout_check(o, "o")
+    _layout_check(x, "x")
+    B, Hs, S, D = o.shape
+    if x.shape[0] != B or x.shape[1] != S or x.shape[3] != D or x.device != o.device:
+        raise ValueError("x must be [B,S,H,D] matching o [B,Hs,S,D] on the same device")
+    st = _load().bnsd_to_bsnd(_ptr(o), _ptr(x), B, S, x.shape[2], h0, Hs, D, _stream())
+    _check("bnsd_to_bsnd", st)
+    return x

@@ -135,6 +135,19 @@ int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_strid
                                            causal != 0, out_dtype == DIT_FP32, workspace, qn, stream));
 }
 
+// Shared checks of the layout entry points: a is the BSND tensor, b the BNSD slice.
+int check_layout(const void* a, const void* b, int B, int S, int H, int h0, int Hs, int D) {
+    if (!a || !b) return DIT_ERR_NULL;
+    if (B < 1 || S < 1 || H < 1 || Hs < 1 || D < 1 || h0 < 0 || h0 > H - Hs) return DIT_ERR_SHAPE;
+    if (D % 8 != 0) return DIT_ERR_UNSUPPORTED;
+    if ((int64_t)B * S * H * D > kMaxElems) return DIT_ERR_SHAPE;
+    if (!aligned(a, 16) || !aligned(b, 16)) return DIT_ERR_ALIGN;
+    const Range rs = range_of(a, (int64_t)B * S * H * D * 2);        // the BSND tensor
+    const Range rn = range_of(b, (int64_t)B * Hs * S * D * 2);       // the BNSD slice
+    if (overlap(rs, rn)) return DIT_ERR_ALIAS;
+    return DIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,6 +228,20 @@ int attn_merge(void* out_a, float* lse_a, const void* out_b, const float* lse_b,
     (void)hipGetLastError();
     return hip_status(dit::launch_attn_merge(out_a, lse_a, out_b, lse_b, rows, D, a_dtype == DIT_FP32,
                                              b_dtype == DIT_FP32, stream));
+}
+
+int bsnd_to_bnsd(const void* x, void* out, int B, int S, int H, int h0, int Hs, int D, hipStream_t stream) {
+    const int st = check_layout(x, out, B, S, H, h0, Hs, D);
+    if (st != DIT_OK) return st;
+    (void)hipGetLastError();
+    return hip_status(dit::launch_layout(x, out, B, S, H, h0, Hs, D, true, stream));
+}
+
+int bnsd_to_bsnd(const void* o, void* x, int B, int S, int H, int h0, int Hs, int D, hipStream_t stream) {
+    const int st = check_layout(x, o, B, S, H, h0, Hs, D);
+    if (st != DIT_OK) return st;
+    (void)hipGetLastError();
+    return hip_status(dit::launch_layout(o, x, B, S, H, h0, Hs, D, false, stream));
 }
 
 const char* dit_attn_status_string(int status) {

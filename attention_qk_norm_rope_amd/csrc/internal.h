@@ -34,6 +34,10 @@ hipError_t launch_qk_norm_rope(void* q, void* k, const float* w_q, const float* 
                                const float* cos_t, const float* sin_t, float eps, int BH, int S,
                                int D, hipStream_t stream);
 
+// BSND [B,S,H,D] head slice [h0, h0+Hs) <-> BNSD [B,Hs,S,D] (2-byte elements).
+hipError_t launch_layout(const void* src, void* dst, int B, int S, int H, int h0, int Hs, int D, bool to_bnsd,
+                         hipStream_t stream);
+
 // out/LSE merge in place into (out_a, lse_a).
 hipError_t launch_attn_merge(void* out_a, float* lse_a, const void* out_b, const float* lse_b,
                              int64_t rows, int D, bool a_f32, bool b_f32, hipStream_t stream);

@@ -54,7 +54,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="wan", choices=["wan", "qwen", "cosmos", "sp"])
+    ap.add_argument("--workload", default="wan", choices=["wan", "qwen", "cosmos", "sp", "ulysses"],
+                    help="ulysses: only the BSND<->BNSD head-slice layout kernels of one rank of a 4-way "
+                         "Ulysses split at the Wan2.2 shape (reported in GB/s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fuse-q", action="store_true",
                     help="wan workload: apply the query RMSNorm+RoPE inside the attention's Q load "
@@ -101,10 +103,60 @@ def traffic_entry(kernel: str, workload: str):
     return e["bytes_per_launch"] if digest == e["sha256"] else None
 
 
+def bench_ulysses(args):
+    """bsnd_to_bnsd + bnsd_to_bsnd of one rank's 10 heads (4-way split) of
+    B1 S75600 H40 D128 bf16: 2 bytes read + 2 written per element each way."""
+    import torch
+    from attention_qk_norm_rope_amd import bnsd_to_bsnd, bsnd_to_bnsd
+    B, S, H, D, P = 1, 75600, 40, 128, 4
+    hs = H // P
+    dev = torch.device("cuda:0")
+    x = torch.randn((B, S, H, D), device=dev).bfloat16()
+    o = torch.empty((B, hs, S, D), dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+
+    def step(e):
+        e[0].record()
+        bsnd_to_bnsd(x, 0, hs, out=o)
+        e[1].record()
+        bnsd_to_bsnd(o, y, 0)
+        e[2].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]  # noqa: E731
+    for _ in range(args.warmup):
+        step(mk())
+    evs = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    nbytes = B * S * hs * D * 2 * 2
+    t_pre = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_post = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    gbs = lambda t: round(nbytes / (t * 1e-3) / 1e9, 1)  # noqa: E731
+    print(json.dumps({
+        "metric": "Ulysses head-slice layout GB/s (auxiliary measurement, not the headline metric)",
+        "value": gbs((t_pre + t_post) / 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "one rank of a 4-way Ulysses split, B1 S75600 H40 D128: 10 heads BSND->BNSD "
+                               "and back"},
+        "kernels": {"bsnd_to_bnsd": {"avg_ms": round(t_pre, 4), "bytes": nbytes, "gbs": gbs(t_pre),
+                                     "frac_hbm_peak": round(nbytes / (t_pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                    "bnsd_to_bsnd": {"avg_ms": round(t_post, 4), "bytes": nbytes, "gbs": gbs(t_post),
+                                     "frac_hbm_peak": round(nbytes / (t_post * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.workload == "ulysses":
+        if args.gpus != 1:
+            print("bench.py measures one GPU only.", file=sys.stderr)
+            sys.exit(2)
+        bench_ulysses(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -7,6 +7,7 @@
  *   attn_fwd_gqa   the same with Hkv K/V heads shared by H query heads
  *   attn_fwd_ws_fused_q  attention with the query prologue fused into its Q load
  *   attn_merge     fold of two partial attentions over disjoint key sets
+ *   bsnd_to_bnsd, bnsd_to_bsnd  head-slice layout change of Ulysses sequence parallelism
  *
  * Sources of the operations (page title, section):
  *   [COSMOS] "Cosmos 昇腾 NPU 多卡并行优化说明": §3.1 fused attention on BNSD
@@ -201,6 +202,28 @@ int attn_fwd_ws_fused_q(const void *q, const void *k, const void *v, int64_t kv_
  */
 int attn_merge(void *out_a, float *lse_a, const void *out_b, const float *lse_b,
                int B, int H, int Sq, int D, int a_dtype, int b_dtype, hipStream_t stream);
+
+/*
+ * Head-slice layout change around the all-to-all of Ulysses sequence
+ * parallelism. [PR274] item 2 (npu_ulysses_attention) gathers the sequence
+ * and splits the heads, runs the fused attention on BNSD, then does the
+ * all-to-all back. [WAN] npu_fused_infer_attention_score produces BNSD that
+ * the caller transposes.
+ *
+ * The model's activations are BSND, x [B,S,H,D]. The attention of the head
+ * slice [h0, h0+Hs) wants BNSD, [B,Hs,S,D]:
+ *   bsnd_to_bnsd:  out[b,h,s,d] = x[b,s,h0+h,d]
+ *   bnsd_to_bsnd:  x[b,s,h0+h,d] = o[b,h,s,d]   (the other heads of x untouched)
+ *
+ * Elements are 2-byte values (bf16) copied bit for bit.
+ *   - D is a multiple of 8.
+ *   - 0 <= h0 <= H - Hs.
+ *   - The BSND tensor and the BNSD slice must not overlap.
+ */
+int bsnd_to_bnsd(const void *x, void *out, int B, int S, int H, int h0, int Hs, int D,
+                 hipStream_t stream);
+int bnsd_to_bsnd(const void *o, void *x, int B, int S, int H, int h0, int Hs, int D,
+                 hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *dit_attn_status_string(int status);

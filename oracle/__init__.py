@@ -14,7 +14,11 @@ Definitions followed (cited by page title and section):
     (rms_norm and rotary_mul sections, interleave mode);
   * out/LSE merge -- Wan2.2 page, "Ring Attention Overlap", and
     "feat: support Ascend NPU backend ... #274", change list item 2
-    (update_out_and_lse).
+    (update_out_and_lse);
+  * BSND <-> BNSD head-slice layout -- #274 change list item 2
+    (npu_ulysses_attention: gather the sequence, split the heads) and the
+    Wan2.2 page (attention output in BNSD, transposed by the caller); written
+    here with numpy indexing.
 
 Every function is pinned by the CPU tests in ``tests/test_oracle_*.py``.
 """
@@ -150,3 +154,26 @@ def merge(out_a, lse_a, out_b, lse_b):
     if rc != 0:
         raise ValueError("oracle_merge rejected its arguments")
     return out, lse
+
+
+def bsnd_to_bnsd(x, h0: int = 0, heads: int | None = None):
+    """out[b, h, s, d] = x[b, s, h0 + h, d] for the head slice [h0, h0+heads)
+    of a BSND array x [B,S,H,D].  Returns a new contiguous [B,heads,S,D]."""
+    x = np.asarray(x)
+    B, S, H, D = x.shape
+    heads = H - h0 if heads is None else heads
+    if not (0 <= h0 and heads >= 1 and h0 + heads <= H):
+        raise ValueError("head slice out of range")
+    return np.ascontiguousarray(x[:, :, h0:h0 + heads, :].transpose(0, 2, 1, 3))
+
+
+def bnsd_to_bsnd(o, x, h0: int = 0):
+    """x[b, s, h0 + h, d] = o[b, h, s, d]; returns a copy of x [B,S,H,D] with
+    that head slice replaced and the other heads as they were."""
+    o = np.asarray(o)
+    y = np.array(x, copy=True)
+    B, Hs, S, D = o.shape
+    if y.shape[0] != B or y.shape[1] != S or y.shape[3] != D or not (0 <= h0 and h0 + Hs <= y.shape[2]):
+        raise ValueError("shape mismatch")
+    y[:, :, h0:h0 + Hs, :] = o.transpose(0, 2, 1, 3)
+    return y

@@ -48,6 +48,8 @@ def lib():
     lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
                                         i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
+    lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
+    lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
     lib.dit_attn_version.restype = ctypes.c_char_p
     return lib
@@ -56,7 +58,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
-                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_merge", "dit_attn_status_string",
+                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd", "dit_attn_status_string",
                           "dit_attn_version"}, names
     for name in names:
         assert hasattr(lib, name), name
@@ -213,3 +215,21 @@ def test_attn_merge_rejections(lib):
     assert f(O, L, O + 4096, W1, 1, 2, 256, 64, BF16, BF16, None) == ALIAS
     assert f(O, O + 1024, V, W1, 1, 2, 256, 64, BF16, BF16, None) == ALIAS
     assert f(O, L, V, L, 1, 2, 256, 64, FP32, BF16, None) == ALIAS
+
+
+@pytest.mark.parametrize("fn", ["bsnd_to_bnsd", "bnsd_to_bsnd"])
+def test_layout_rejections(lib, fn):
+    f = getattr(lib, fn)
+    X, Y = 0x30_0000_0000, 0x40_0000_0000
+    assert f(None, Y, 1, 8, 4, 0, 2, 128, None) == NULL
+    assert f(X, None, 1, 8, 4, 0, 2, 128, None) == NULL
+    assert f(X, Y, 1, 8, 4, 3, 2, 128, None) == SHAPE        # slice past the last head
+    assert f(X, Y, 1, 8, 4, -1, 2, 128, None) == SHAPE
+    assert f(X, Y, 1, 8, 4, 0, 0, 128, None) == SHAPE
+    assert f(X, Y, 0, 8, 4, 0, 2, 128, None) == SHAPE
+    assert f(X, Y, 1, 8, 4, 0, 2, 60, None) == UNSUP         # D not a multiple of 8
+    assert f(X + 2, Y, 1, 8, 4, 0, 2, 128, None) == ALIGN
+    # the BNSD slice inside the BSND tensor (bsnd_to_bnsd takes the BSND side
+    # first, bnsd_to_bsnd second)
+    src, dst = (X, X + 4096) if fn == "bsnd_to_bnsd" else (X + 4096, X)
+    assert f(src, dst, 1, 8, 4, 0, 2, 128, None) == ALIAS
