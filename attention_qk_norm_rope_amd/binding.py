@@ -52,10 +52,11 @@ def _load():
     lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
                                         i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
+    lib.attn_fwd_varlen.argtypes = [p, p, p, p, i64, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_fwd_ws_fused_q",
-                 "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd"):
+                 "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -255,6 +256,34 @@ def attn_fwd_gqa(q, k, v, workspace=None, out=None, lse=None, scale: float | Non
     st = _load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), sk, ws_ptr, ws_bytes, _ptr(out), _ptr(lse), B, H, Hkv,
                               Sq, Skv, D, scale, 1 if causal else 0, _dtype_code(out), _stream())
     _check("attn_fwd_gqa", st)
+    return out, lse
+
+
+def attn_fwd_varlen(q, k, v, seqlens_q, seqlens_kv, workspace=None, out=None, lse=None,
+                    scale: float | None = None, causal: bool = False, out_dtype=torch.bfloat16,
+                    return_lse: bool = True):
+    """Attention over padded batches: q bf16 [B,H,Sq,D]; k, v bf16
+    [B,Hkv,Skv,D] contiguous; seqlens_q / seqlens_kv int32 [B] device tensors
+    (valid query rows / keys per batch).  Padding rows get out = 0 and
+    lse = -inf.  Optional workspace as in attn_fwd_gqa.  Returns (out, lse)."""
+    if k.dim() != 4 or not k.is_contiguous() or not v.is_contiguous():
+        raise ValueError("k and v must be contiguous [B,Hkv,Skv,D]")
+    Hkv = k.shape[1]
+    (B, H, Sq, Skv, D), sk, scale, out, lse = _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse,
+                                                         kv_heads=Hkv)
+    for t, name in ((seqlens_q, "seqlens_q"), (seqlens_kv, "seqlens_kv")):
+        _need(t, name, torch.int32, q.device)
+        if tuple(t.shape) != (B,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous int32 [{B}]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = _load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), ws_ptr, ws_bytes, _ptr(out), _ptr(lse),
+                                 _ptr(seqlens_q), _ptr(seqlens_kv), B, H, Hkv, Sq, Skv, D, scale,
+                                 1 if causal else 0, _dtype_code(out), _stream())
+    _check("attn_fwd_varlen", st)
     return out, lse
 
 

@@ -180,19 +180,23 @@ __device__ __forceinline__ unsigned p_pair(float s0, float s1, float c, float ne
 }
 
 // O /= l, store the row (bf16 or fp32) and LSE = ln2 * (m + log2 l).
+// A padding row (pad) and a row that saw no key (l = 0) store zeros and
+// LSE = -inf.
 template <int D, bool OUT_F32>
 __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run, float l_half, int64_t row,
-                                          bool valid, int hh, void* out, float* lse) {
+                                          bool valid, bool pad, int hh, void* out, float* lse) {
     const float l = pair_sum(l_half);
-    const float inv = 1.0f / l;
+    const bool empty = pad || !(l > 0.f);
+    const float inv = empty ? 0.f : 1.0f / l;
     if (!valid) return;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d = 32 * db + 8 * g + 4 * hh;
-            const float a0 = o[db][4 * g + 0] * inv, a1 = o[db][4 * g + 1] * inv;
-            const float a2 = o[db][4 * g + 2] * inv, a3 = o[db][4 * g + 3] * inv;
+            float a0 = o[db][4 * g + 0] * inv, a1 = o[db][4 * g + 1] * inv;
+            float a2 = o[db][4 * g + 2] * inv, a3 = o[db][4 * g + 3] * inv;
+            if (empty) a0 = a1 = a2 = a3 = 0.f;   // not 0 * (garbage of padding rows)
             if constexpr (OUT_F32) {
                 f32x4 w = {a0, a1, a2, a3};
                 *(f32x4*)((float*)out + row * D + d) = w;
@@ -202,7 +206,7 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run
             }
         }
     // v_log_f32 is log2.
-    if (lse && hh == 0) lse[row] = (m_run + __builtin_amdgcn_logf(l)) * LN2;
+    if (lse && hh == 0) lse[row] = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l)) * LN2;
 }
 
 // ---------------------------------------------------------------------------
@@ -217,8 +221,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, int64_t kv_bh_stride, void* __restrict__ out,
-                float* __restrict__ lse, int Sq, int Skv, float c, unsigned qsign, int causal,
-                int n_qtiles, int H, int G) {
+                float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
+                int n_qtiles, int H, int G, const int* __restrict__ lq, const int* __restrict__ lkv) {
     constexpr int BM = GEN_WAVES * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int KDMA = BN * D * 2 / 1024 / GEN_WAVES;  // 1 KB DMA chunks per wave per tile
@@ -236,6 +240,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = logical / n_qtiles;
     const int bkv = kv_head(bh, H, G);
+    // Per-batch valid lengths (variable-length batches): query rows >= Sq_b
+    // are padding, keys >= Skv are masked.  Both clamp to the tensor sizes.
+    const int Sq_b = lq ? min(max(lq[bh / H], 0), Sq) : Sq;
+    const int Skv = lkv ? min(max(lkv[bh / H], 0), Skv_all) : Skv_all;
     int qt = logical - bh * n_qtiles;
     if (causal) qt = n_qtiles - 1 - qt;   // longest rows first
     const int q0 = qt * BM;
@@ -263,9 +271,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     int n_tiles = (Skv + BN - 1) / BN;
     if (causal) {
-        const int qlast = min(q0 + BM, Sq) - 1;
+        const int qlast = min(q0 + BM, Sq_b) - 1;
         n_tiles = min(n_tiles, qlast / BN + 1);
     }
+    if (q0 >= Sq_b) n_tiles = 0;       // a tile of padding rows only
 
     // K tile -> Kbuf by DMA.  Wave w fills 1 KB chunks w*KDMA .. w*KDMA+KDMA-1;
     // lane l of a chunk lands at byte 16*l of it, i.e. linear 16-byte slot
@@ -415,7 +424,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (j < n_tiles) step(B0{}, j, sA, sB);
 
     const int qi = q0w + n;
-    store_row<D, OUT_F32>(o, m_run, l_run, (int64_t)bh * Sq + qi, qi < Sq, hh, out, lse);
+    store_row<D, OUT_F32>(o, m_run, l_run, (int64_t)bh * Sq + qi, qi < Sq, qi >= Sq_b, hh, out, lse);
 }
 
 // ---------------------------------------------------------------------------
@@ -433,8 +442,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(WS_WAVES * 64, WS_WAV
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
-                   float* __restrict__ lse, int Sq, int Skv, float c, unsigned qsign, int causal,
-                   int n_qtiles, int H, int G, QNormRope qn) {
+                   float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
+                   int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
+                   const int* __restrict__ lkv) {
     constexpr int BM = WS_WAVES * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int TILE = BN * D;                         // elements of one K or V tile
@@ -451,6 +461,10 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = logical / n_qtiles;
     const int bkv = kv_head(bh, H, G);
+    // Per-batch valid lengths (variable-length batches): query rows >= Sq_b
+    // are padding, keys >= Skv are masked.  Both clamp to the tensor sizes.
+    const int Sq_b = lq ? min(max(lq[bh / H], 0), Sq) : Sq;
+    const int Skv = lkv ? min(max(lkv[bh / H], 0), Skv_all) : Skv_all;
     int qt = logical - bh * n_qtiles;
     if (causal) qt = n_qtiles - 1 - qt;
     const int q0 = qt * BM;
@@ -459,7 +473,7 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // wave is uniform: kept scalar so the DMA's LDS address (M0) needs no VALU.
     const int wave = uniform_int(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
     const int q0w = q0 + wave * QPW;
-    const int n_vt = (Skv + BN - 1) / BN;
+    const int n_vt = (Skv_all + BN - 1) / BN;     // tiles of the V image
 
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(q + (int64_t)bh * Sq * D), (short)0, Sq * D * 2, RSRC_WORD3);
@@ -529,11 +543,12 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
     }
 
-    int n_tiles = n_vt;
+    int n_tiles = (Skv + BN - 1) / BN;
     if (causal) {
-        const int qlast = min(q0 + BM, Sq) - 1;
+        const int qlast = min(q0 + BM, Sq_b) - 1;
         n_tiles = min(n_tiles, qlast / BN + 1);
     }
+    if (q0 >= Sq_b) n_tiles = 0;       // a tile of padding rows only
 
     // DMA sources: a buffer resource per tile, based at the tile (scalar
     // arithmetic), so every lane's offset is loop-invariant; the resource
@@ -711,13 +726,13 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
 
     const int qi = q0w + n;
-    store_row<D, OUT_F32>(o, m_run, l_run, (int64_t)bh * Sq + qi, qi < Sq, hh, out, lse);
+    store_row<D, OUT_F32>(o, m_run, l_run, (int64_t)bh * Sq + qi, qi < Sq, qi >= Sq_b, hh, out, lse);
 }
 
 template <int D, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
                   int BH, int H, int G, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
-                  const QNormRope* qn, hipStream_t stream) {
+                  const QNormRope* qn, const int* lq, const int* lkv, hipStream_t stream) {
     const int waves = vws ? WS_WAVES : GEN_WAVES;
     const int BM = waves * QPW;
     const int n_qtiles = (Sq + BM - 1) / BM;
@@ -726,15 +741,15 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
     if (vws && qn)
         hipLaunchKernelGGL((attn_fwd_ws_kernel<D, OUT_F32, true>), dim3((unsigned)nblk), dim3(WS_WAVES * 64), 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vws, kv_bh_stride, out,
-                           lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, *qn);
+                           lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, *qn, lq, lkv);
     else if (vws)
         hipLaunchKernelGGL((attn_fwd_ws_kernel<D, OUT_F32, false>), dim3((unsigned)nblk), dim3(WS_WAVES * 64), 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vws, kv_bh_stride, out,
-                           lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, QNormRope{});
+                           lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, QNormRope{}, lq, lkv);
     else
         hipLaunchKernelGGL((attn_fwd_kernel<D, OUT_F32>), dim3((unsigned)nblk), dim3(GEN_WAVES * 64), 0, stream,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, kv_bh_stride, out, lse,
-                           Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G);
+                           Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, lq, lkv);
     return hipGetLastError();
 }
 
@@ -742,7 +757,8 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
-                           bool causal, bool out_f32, const void* vws, const QNormRope* qn, hipStream_t stream) {
+                           bool causal, bool out_f32, const void* vws, const QNormRope* qn, const int* lq,
+                           const int* lkv, hipStream_t stream) {
     // Positive multiplier for exp2; the sign of the scale goes into Q.  A
     // zero (or vanishing) scale keeps a tiny positive multiplier so that
     // masked logits (-inf) still map to probability 0; the logits it yields
@@ -751,10 +767,10 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
     if (!(c >= 1e-30f)) c = 1e-30f;
     const unsigned qsign = scale < 0.f ? 0x80008000u : 0u;
     if (D == 128)
-        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, stream)
-                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, stream);
-    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, stream)
-                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, stream);
+        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, stream)
+                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, stream);
+    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, stream)
+                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, stream);
 }
 
 }  // namespace dit

@@ -105,7 +105,8 @@ int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride
 // optional fused Q prologue (workspace path only), Hkv K/V heads.
 int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
                 int64_t workspace_bytes, void* out, float* lse, int B, int H, int Hkv, int Sq, int Skv, int D,
-                float scale, int causal, int out_dtype, const dit::QNormRope* qn, hipStream_t stream) {
+                float scale, int causal, int out_dtype, const dit::QNormRope* qn, const int* lq, const int* lkv,
+                hipStream_t stream) {
     AttnRanges r;
     const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Hkv, Sq, Skv, D, scale, out_dtype, &r);
     if (st != DIT_OK) return st;
@@ -126,13 +127,22 @@ int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_strid
                 if (overlap(t, r.out) || overlap(t, rw) || (lse && overlap(t, r.lse))) return DIT_ERR_ALIAS;
         }
     }
+    if (lq || lkv) {
+        if (!lq || !lkv) return DIT_ERR_NULL;
+        if (!aligned(lq, 4) || !aligned(lkv, 4)) return DIT_ERR_ALIGN;
+        const Range rl[2] = {range_of(lq, (int64_t)B * 4), range_of(lkv, (int64_t)B * 4)};
+        for (const Range& t : rl)
+            if (overlap(t, r.out) || (lse && overlap(t, r.lse)) ||
+                (workspace && overlap(t, range_of(workspace, attn_fwd_workspace_bytes(B, Hkv, Skv, D)))))
+                return DIT_ERR_ALIAS;
+    }
     (void)hipGetLastError();
     if (workspace) {
-        const hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * Hkv, Skv, D, stream);
+        const hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * Hkv, Skv, D, lkv, Hkv, stream);
         if (e != hipSuccess) return DIT_ERR_HIP;
     }
     return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, H, H / Hkv, Sq, Skv, D, scale,
-                                           causal != 0, out_dtype == DIT_FP32, workspace, qn, stream));
+                                           causal != 0, out_dtype == DIT_FP32, workspace, qn, lq, lkv, stream));
 }
 
 // Shared checks of the layout entry points: a is the BSND tensor, b the BNSD slice.
@@ -182,7 +192,7 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, int64_t kv_bh_stri
                  int64_t workspace_bytes, void* out, float* lse, int B, int H, int Hkv, int Sq, int Skv, int D,
                  float scale, int causal, int out_dtype, hipStream_t stream) {
     return attn_common(q, k, v, kv_bh_stride, workspace, workspace_bytes, out, lse, B, H, Hkv, Sq, Skv, D, scale,
-                       causal, out_dtype, nullptr, stream);
+                       causal, out_dtype, nullptr, nullptr, nullptr, stream);
 }
 
 int attn_fwd_ws_fused_q(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
@@ -199,7 +209,20 @@ int attn_fwd_ws_fused_q(const void* q, const void* k, const void* v, int64_t kv_
     if ((int64_t)Sq * D * 4 > 0x7FFFFFFF) return DIT_ERR_SHAPE;
     const dit::QNormRope qn{w_q, cos_q, sin_q, eps};
     return attn_common(q, k, v, kv_bh_stride, workspace, workspace_bytes, out, lse, B, H, H, Sq, Skv, D, scale,
-                       causal, out_dtype, &qn, stream);
+                       causal, out_dtype, &qn, nullptr, nullptr, stream);
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* workspace, int64_t workspace_bytes,
+                    void* out, float* lse, const int* seqlens_q, const int* seqlens_kv, int B, int H, int Hkv,
+                    int Sq, int Skv, int D, float scale, int causal, int out_dtype, hipStream_t stream) {
+    if (!seqlens_q || !seqlens_kv) {
+        AttnRanges r;
+        const int st = check_attn(q, k, v, (int64_t)Skv * D, out, lse, B, H, Hkv, Sq, Skv, D, scale, out_dtype, &r);
+        return st != DIT_OK ? st : DIT_ERR_NULL;
+    }
+    if (Skv < 1 || D < 1) return !q || !k || !v || !out ? DIT_ERR_NULL : DIT_ERR_SHAPE;
+    return attn_common(q, k, v, (int64_t)Skv * D, workspace, workspace_bytes, out, lse, B, H, Hkv, Sq, Skv, D,
+                       scale, causal, out_dtype, nullptr, seqlens_q, seqlens_kv, stream);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Sq,

@@ -11,7 +11,9 @@ namespace dit {
 // bh = b*H + h reads K/V head g = b*(H/G) + h/G, rows at k + g*kv_bh_stride
 // + j*D (G = 1: g = bh).  With vws != null, V is read from the prepared tiles
 // written by launch_v_prep over the B*H/G K/V heads.
-// With qn != null (workspace path only), q holds the raw rows and the kernel
+// With lq, lkv != null (device int32 [B]), batch b has lq[b] query rows and
+// lkv[b] keys (clamped to [0, Sq] and [0, Skv]); padding rows store zeros and
+// LSE -inf.  With qn != null (workspace path only), q holds the raw rows and the kernel
 // applies the per-head RMSNorm + interleaved rotary of qk_norm_rope to them
 // as it loads them (same bits as running qk_norm_rope on q first).
 struct QNormRope {
@@ -22,12 +24,14 @@ struct QNormRope {
 };
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
-                           bool causal, bool out_f32, const void* vws, const QNormRope* qn, hipStream_t stream);
+                           bool causal, bool out_f32, const void* vws, const QNormRope* qn, const int* lq,
+                           const int* lkv, hipStream_t stream);
 
 // Bytes of prepared V for BH heads of Skv keys; launch_v_prep writes them.
 int64_t v_prep_bytes(int64_t BH, int Skv, int D);
-hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D,
-                         hipStream_t stream);
+// With lkv != null, head bh (of B*Hkv) keeps keys < lkv[bh / Hkv] and zeros the rest.
+hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D, const int* lkv,
+                         int Hkv, hipStream_t stream);
 
 // RMSNorm + interleaved rotary, in place; q or k may be null.
 hipError_t launch_qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k,

@@ -42,7 +42,7 @@ __device__ __forceinline__ unsigned pick_pair_f16(const u32x4& a, const u32x4& b
 template <int D>
 __global__ void __launch_bounds__(256)
 v_prep_kernel(const uint16_t* __restrict__ v, int64_t kv_bh_stride, uint16_t* __restrict__ ws, int BH,
-              int Skv, int n_tiles) {
+              int Skv, int n_tiles, const int* __restrict__ lkv, int Hkv) {
     constexpr int TILE = BN * D;                 // elements per tile image
     __shared__ __attribute__((aligned(16))) uint16_t img[TILE];
     const int tile = blockIdx.x, tid = threadIdx.x;
@@ -52,8 +52,10 @@ v_prep_kernel(const uint16_t* __restrict__ v, int64_t kv_bh_stride, uint16_t* __
     const int lslot = col >> 3, sub = col & 7;
     // grid.y is capped at 65535; heads beyond it are taken in turn.
     for (int bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+        // Keys past this head's valid length read as zeros.
+        const int len = lkv ? min(max(lkv[bh / Hkv], 0), Skv) : Skv;
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(v + (int64_t)bh * kv_bh_stride), (short)0, Skv * D * 2, RSRC_WORD3);
+            (void*)(v + (int64_t)bh * kv_bh_stride), (short)0, len * D * 2, RSRC_WORD3);
         if (dc < D / 8) {
             const int key0 = tile * BN + 4 * kg;
             u32x4 r[4];
@@ -79,11 +81,12 @@ v_prep_kernel(const uint16_t* __restrict__ v, int64_t kv_bh_stride, uint16_t* __
 }
 
 template <int D>
-hipError_t launch(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, hipStream_t stream) {
+hipError_t launch(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, const int* lkv, int Hkv,
+                  hipStream_t stream) {
     const int n_tiles = (Skv + BN - 1) / BN;
     const unsigned gy = (unsigned)(BH < 65535 ? BH : 65535);
     hipLaunchKernelGGL((v_prep_kernel<D>), dim3((unsigned)n_tiles, gy), dim3(256), 0, stream,
-                       (const uint16_t*)v, kv_bh_stride, (uint16_t*)ws, BH, Skv, n_tiles);
+                       (const uint16_t*)v, kv_bh_stride, (uint16_t*)ws, BH, Skv, n_tiles, lkv, Hkv);
     return hipGetLastError();
 }
 
@@ -94,10 +97,10 @@ int64_t v_prep_bytes(int64_t BH, int Skv, int D) {
     return BH * n_tiles * BN * D * 2;
 }
 
-hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D,
-                         hipStream_t stream) {
-    if (D == 128) return launch<128>(v, kv_bh_stride, ws, BH, Skv, stream);
-    return launch<64>(v, kv_bh_stride, ws, BH, Skv, stream);
+hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D, const int* lkv,
+                         int Hkv, hipStream_t stream) {
+    if (D == 128) return launch<128>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, stream);
+    return launch<64>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, stream);
 }
 
 }  // namespace dit

@@ -5,6 +5,7 @@
  *   qk_norm_rope   per-head RMSNorm of q and k, then interleaved rotary, in place
  *   attn_fwd       softmax(scale * Q K^T) V with a per-row log-sum-exp (BNSD)
  *   attn_fwd_gqa   the same with Hkv K/V heads shared by H query heads
+ *   attn_fwd_varlen  the same over padded batches with per-batch lengths
  *   attn_fwd_ws_fused_q  attention with the query prologue fused into its Q load
  *   attn_merge     fold of two partial attentions over disjoint key sets
  *   bsnd_to_bnsd, bnsd_to_bsnd  head-slice layout change of Ulysses sequence parallelism
@@ -164,6 +165,31 @@ int attn_fwd_gqa(const void *q, const void *k, const void *v, int64_t kv_bh_stri
                  void *workspace, int64_t workspace_bytes, void *out, float *lse,
                  int B, int H, int Hkv, int Sq, int Skv, int D, float scale, int causal,
                  int out_dtype, hipStream_t stream);
+
+/*
+ * Variable-length batches: [WAN] npu_fused_infer_attention_score takes
+ * actual_seq_lengths and actual_seq_lengths_kv. q, k and v are padded
+ * tensors: q [B,H,Sq,D], k and v [B,Hkv,Skv,D] contiguous (Hkv as in
+ * attn_fwd_gqa). Batch b holds seqlens_q[b] valid query rows and
+ * seqlens_kv[b] valid keys.
+ *
+ * Valid rows attend to the valid keys only; causal means j <= i as in
+ * attn_fwd. Padding rows (i >= seqlens_q[b]) and rows that see no key store
+ * out = 0 and lse = -inf, so a later attn_merge ignores them.
+ *
+ *   seqlens_q, seqlens_kv  device int32 [B], 4-byte aligned, read by the
+ *                          kernels on the stream. Values are clamped to
+ *                          [0, Sq] and [0, Skv]; they are not checked on the
+ *                          host. Neither may overlap out, lse or the workspace.
+ *   workspace              optional, as in attn_fwd_gqa.
+ *
+ * Other arguments and errors are as for attn_fwd_gqa with
+ * kv_bh_stride = Skv*D.
+ */
+int attn_fwd_varlen(const void *q, const void *k, const void *v, void *workspace,
+                    int64_t workspace_bytes, void *out, float *lse, const int *seqlens_q,
+                    const int *seqlens_kv, int B, int H, int Hkv, int Sq, int Skv, int D,
+                    float scale, int causal, int out_dtype, hipStream_t stream);
 
 /*
  * attn_fwd_ws with the query half of qk_norm_rope fused into the attention's

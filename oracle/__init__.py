@@ -177,3 +177,28 @@ def bnsd_to_bsnd(o, x, h0: int = 0):
         raise ValueError("shape mismatch")
     y[:, :, h0:h0 + Hs, :] = o.transpose(0, 2, 1, 3)
     return y
+
+
+def attn_varlen(q, k, v, seqlens_q, seqlens_kv, scale: float, causal: bool = False):
+    """Attention over padded batches, from the definition: batch b is full
+    attention of its first seqlens_q[b] query rows over its first
+    seqlens_kv[b] keys (K/V head h // (H // Hkv) for query head h); padding
+    rows, and rows that see no key, are 0 with LSE -inf.  q [B,H,Sq,D], k, v
+    [B,Hkv,Skv,D] bf16 bits.  Returns fp64 out [B,H,Sq,D], lse [B,H,Sq]."""
+    q, k, v = _bits(q, "q"), _bits(k, "k"), _bits(v, "v")
+    B, H, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    out = np.zeros((B, H, Sq, D), dtype=np.float64)
+    lse = np.full((B, H, Sq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        lq = int(min(max(seqlens_q[b], 0), Sq))
+        lk = int(min(max(seqlens_kv[b], 0), Skv))
+        if lq == 0 or lk == 0:
+            continue
+        kb = np.repeat(k[b:b + 1, :, :lk], H // Hkv, axis=1)
+        vb = np.repeat(v[b:b + 1, :, :lk], H // Hkv, axis=1)
+        o, l = attn(np.ascontiguousarray(q[b:b + 1, :, :lq]), np.ascontiguousarray(kb), np.ascontiguousarray(vb),
+                    scale, causal)
+        out[b, :, :lq] = o[0]
+        lse[b, :, :lq] = l[0]
+    return out, lse

@@ -48,6 +48,7 @@ def lib():
     lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
                                         i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
+    lib.attn_fwd_varlen.argtypes = [p, p, p, p, i64, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -58,7 +59,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
-                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd", "dit_attn_status_string",
+                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd",
+                          "bnsd_to_bsnd", "dit_attn_status_string",
                           "dit_attn_version"}, names
     for name in names:
         assert hasattr(lib, name), name
@@ -233,3 +235,18 @@ def test_layout_rejections(lib, fn):
     # first, bnsd_to_bsnd second)
     src, dst = (X, X + 4096) if fn == "bsnd_to_bnsd" else (X + 4096, X)
     assert f(src, dst, 1, 8, 4, 0, 2, 128, None) == ALIAS
+
+
+def test_attn_fwd_varlen_rejections(lib):
+    f = lib.attn_fwd_varlen
+    LQ, LK = 0x50_0000_0000, 0x50_0000_1000
+
+    def call(lq=LQ, lk=LK, Hkv=2, o=O):
+        return f(Q, K, V, None, 0, o, L, lq, lk, 1, 2, Hkv, 256, 256, 64, 0.125, 0, BF16, None)
+
+    assert call(lq=None) == NULL
+    assert call(lk=None) == NULL
+    assert call(lq=LQ + 2) == ALIGN
+    assert call(lk=O) == ALIAS                           # lengths on the output
+    assert call(Hkv=3) == SHAPE
+    assert call(o=None) == NULL
