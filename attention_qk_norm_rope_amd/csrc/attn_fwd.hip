@@ -4,16 +4,16 @@
 //
 // Operation: "Cosmos 昇腾 NPU 多卡并行优化说明" §3.1 and the
 // npu_fused_infer_attention_score section of "NPU Wan2.2-I2V模型推理优化实践"
-// (BNSD, explicit softmax scale, full or top-left causal attention); the LSE
-// is the statistic the Ring Attention Overlap section merges with.
+// (BNSD, explicit softmax scale, full or top-left causal attention, key/value
+// head groups, per-batch valid lengths); the LSE is the statistic the Ring
+// Attention Overlap section merges with.
 //
-// Two kernels share one arithmetic design:
-//  * attn_fwd_kernel: 4 waves x 32 query rows; V is loaded through registers
-//    and transposed into LDS each tile (needs no workspace).
-//  * attn_fwd_ws_kernel: 8 waves x 32 query rows; V comes from a workspace
-//    that v_prep_kernel filled with fp16 V^T tile images, copied into LDS by
-//    the buffer->LDS DMA like K.  The 8 waves share each K/V tile, which
-//    halves the L2->LDS traffic per FLOP.
+// One kernel, 8 waves x 32 query rows per workgroup, with two sources of V:
+//  * VPREP: v_prep_kernel wrote fp16 V^T tile images into a workspace, and
+//    they are copied into LDS by the buffer->LDS DMA like K (attn_fwd_ws);
+//  * otherwise each iteration loads the V tile into registers and writes it
+//    into LDS in the same image layout (attn_fwd, no workspace).
+// The 8 waves share each K/V tile in LDS.
 //
 // Arithmetic design:
 //  * Scores are computed transposed, S^T = K Q^T, with
@@ -75,8 +75,7 @@ using B1 = std::integral_constant<int, 1>;
 
 constexpr int BN = 64;                 // keys per tile
 constexpr int QPW = 32;                // query rows per wave
-constexpr int GEN_WAVES = 4;           // waves per workgroup, attn_fwd_kernel
-constexpr int WS_WAVES = 8;            // waves per workgroup, attn_fwd_ws_kernel
+constexpr int WAVES = 8;               // waves per workgroup
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float TAU = 8.0f;            // lazy-rescale threshold, log2 units
 constexpr int RSRC_WORD3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
@@ -210,226 +209,7 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run
 }
 
 // ---------------------------------------------------------------------------
-// attn_fwd_kernel: V through registers.  Software pipeline, one barrier per
-// 64-key tile: while the softmax of tile j runs on the VALU, the MFMAs of
-// tile j+1's scores are in flight; iteration j DMAs K_{j+2} straight into
-// LDS and loads V_{j+1} into registers, transposing it into LDS at the end.
-// V^T rows are padded to BN+8 keys (144 bytes), which spreads 16 consecutive
-// rows over distinct bank groups.
-template <int D, bool OUT_F32>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256)))
-__attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                const uint16_t* __restrict__ v, int64_t kv_bh_stride, void* __restrict__ out,
-                float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
-                int n_qtiles, int H, int G, const int* __restrict__ lq, const int* __restrict__ lkv) {
-    constexpr int BM = GEN_WAVES * QPW;
-    constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
-    constexpr int KDMA = BN * D * 2 / 1024 / GEN_WAVES;  // 1 KB DMA chunks per wave per tile
-    constexpr int VROW = BN + 8;
-    constexpr int VKG = BN / 4;         // 4-key groups per V tile
-    static_assert(KDMA >= 1, "tile shape");
-
-    __shared__ __attribute__((aligned(16))) uint16_t Ks0[BN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Ks1[BN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt0[D * VROW];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt1[D * VROW];
-    auto Kbuf = [&](auto bc) -> uint16_t* { if constexpr (decltype(bc)::value == 0) return Ks0; else return Ks1; };
-    auto Vbuf = [&](auto bc) -> uint16_t* { if constexpr (decltype(bc)::value == 0) return Vt0; else return Vt1; };
-
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = logical / n_qtiles;
-    const int bkv = kv_head(bh, H, G);
-    // Per-batch valid lengths (variable-length batches): query rows >= Sq_b
-    // are padding, keys >= Skv are masked.  Both clamp to the tensor sizes.
-    const int Sq_b = lq ? min(max(lq[bh / H], 0), Sq) : Sq;
-    const int Skv = lkv ? min(max(lkv[bh / H], 0), Skv_all) : Skv_all;
-    int qt = logical - bh * n_qtiles;
-    if (causal) qt = n_qtiles - 1 - qt;   // longest rows first
-    const int q0 = qt * BM;
-
-    const int tid = threadIdx.x;
-    const int wave = uniform_int(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
-    const int q0w = q0 + wave * QPW;
-
-    // Buffer resources: loads past the end of a (b,h) slab read as zero.
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(q + (int64_t)bh * Sq * D), (short)0, Sq * D * 2, RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(k + (int64_t)bkv * kv_bh_stride), (short)0, Skv * D * 2, RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(v + (int64_t)bkv * kv_bh_stride), (short)0, Skv * D * 2, RSRC_WORD3);
-
-    // Q^T fragments: lane holds query (q0w + n), d = 16t + 8hh .. +7.
-    bf16x8 qf[DT];
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, ((q0w + n) * D + 16 * t + 8 * hh) * 2, 0, 0);
-        x ^= qsign;
-        qf[t] = __builtin_bit_cast(bf16x8, x);
-    }
-
-    int n_tiles = (Skv + BN - 1) / BN;
-    if (causal) {
-        const int qlast = min(q0 + BM, Sq_b) - 1;
-        n_tiles = min(n_tiles, qlast / BN + 1);
-    }
-    if (q0 >= Sq_b) n_tiles = 0;       // a tile of padding rows only
-
-    // K tile -> Kbuf by DMA.  Wave w fills 1 KB chunks w*KDMA .. w*KDMA+KDMA-1;
-    // lane l of a chunk lands at byte 16*l of it, i.e. linear 16-byte slot
-    // s = 64*chunk + l = key*SL + (source slot ^ kswz(key)).
-    auto dma_k = [&](int kv0, auto b) {
-#pragma unroll
-        for (int i = 0; i < KDMA; ++i) {
-            const int chunk = wave * KDMA + i;
-            const int s = chunk * 64 + lane;
-            const int key = s / SL;
-            const int slot = (s % SL) ^ kswz<D>(key);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Kbuf(b) + chunk * 512), 16,
-                                                     ((kv0 + key) * D + 8 * slot) * 2, 0, 0, 0);
-        }
-    };
-
-    // V tile: thread (v_kg, v_dc) loads keys 4*v_kg..+3, d 8*v_dc..+7, and
-    // writes them transposed (fp16) into Vbuf[d][vt_col(key)].
-    const int v_kg = tid % VKG, v_dc = tid / VKG;
-    const bool v_active = v_dc < D / 8;
-    u32x4 vst[4];
-    auto load_v = [&](int kv0) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            vst[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((kv0 + 4 * v_kg + kk) * D + 8 * v_dc) * 2, 0, 0);
-    };
-    auto store_v = [&](auto b) {
-        if (v_active) {
-            const int col = vt_col(4 * v_kg);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                u32x2 w2 = {pick_pair_f16(vst[0], vst[1], e), pick_pair_f16(vst[2], vst[3], e)};
-                *(u32x2*)(Vbuf(b) + (8 * v_dc + e) * VROW + col) = w2;
-            }
-        }
-    };
-
-    // S^T = K Q^T for the keys in Kbuf(b); K fragments are read one k-step ahead.
-    auto kfrag = [&](auto b, int kb, int t) {
-        const int key = 32 * kb + n;
-        const int slot = (2 * t + hh) ^ kswz<D>(key);
-        return __builtin_bit_cast(bf16x8, *(const u32x4*)(Kbuf(b) + key * D + 8 * slot));
-    };
-    auto qk = [&](auto b, f32x16 (&s)[KB]) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-        bf16x8 kf[2][KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[0][kb] = kfrag(b, kb, 0);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            if (t + 1 < DT) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) kf[(t + 1) & 1][kb] = kfrag(b, kb, t + 1);
-            }
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t & 1][kb], qf[t], s[kb], 0, 0, 0);
-        }
-    };
-    auto needs_mask = [&](int kv0) { return (kv0 + BN > Skv) || (causal && kv0 + BN - 1 > q0w); };
-
-    f32x16 o[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-
-    // One pipelined iteration: scores of tile j are in sc; leaves tile j+1's
-    // (masked) scores in sn.
-    auto step = [&](auto b, int j, f32x16 (&sc)[KB], f32x16 (&sn)[KB]) {
-        const std::integral_constant<int, 1 - decltype(b)::value> nb{};
-        const int kv0 = j * BN;
-        dma_k(kv0 + 2 * BN, b);        // K_{j+2} (zeros past the end) -> the buffer K_j used
-        load_v(kv0 + BN);              // V_{j+1}
-        qk(nb, sn);                    // S_{j+1}: MFMAs overlap the softmax below
-
-        float alpha;
-        bool grow;
-        tile_max(sc, c, m_run, alpha, grow);
-        const float neg_m = -m_run;
-        float lsum = 0.f;
-        f16x8 pf[KB][2];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                u32x4 w4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w4[e] = p_pair(sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1], c, neg_m, lsum);
-                pf[kb][u] = __builtin_bit_cast(f16x8, w4);
-            }
-        l_run = __builtin_fmaf(l_run, alpha, lsum);
-        // The rescale branch tests a value computed after P (l is never
-        // negative), so the compiler keeps it below the softmax instead of
-        // splitting the block above it.
-        if (__any(grow && l_run >= 0.f)) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        }
-
-        // O^T += V^T P^T (V^T fragments read one step ahead)
-        constexpr int NV = KB * 2 * DB;
-        auto vfrag = [&](int idx) {
-            const int kb = idx / (2 * DB), u = (idx / DB) % 2, db = idx % DB;
-            return __builtin_bit_cast(
-                f16x8, *(const u32x4*)(Vbuf(b) + (32 * db + n) * VROW + 32 * kb + 16 * u + 8 * hh));
-        };
-        f16x8 vf[2];
-        vf[0] = vfrag(0);
-#pragma unroll
-        for (int idx = 0; idx < NV; ++idx) {
-            if (idx + 1 < NV) vf[(idx + 1) & 1] = vfrag(idx + 1);
-            const int kb = idx / (2 * DB), u = (idx / DB) % 2, db = idx % DB;
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[idx & 1], pf[kb][u], o[db], 0, 0, 0);
-        }
-
-        store_v(nb);                   // V_{j+1} -> the buffer V_{j-1} used
-        if (needs_mask(kv0 + BN)) mask_tile(sn, kv0 + BN, Skv, causal, q0w + n, hh);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K_{j+2} has landed in LDS
-        __syncthreads();
-    };
-
-    // Prologue: K_0, K_1 by DMA, V_0 through registers, scores of tile 0.
-    f32x16 sA[KB], sB[KB];
-    dma_k(0, B0{});
-    dma_k(BN, B1{});
-    load_v(0);
-    store_v(B0{});
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    qk(B0{}, sA);
-    if (needs_mask(0)) mask_tile(sA, 0, Skv, causal, q0w + n, hh);
-    __syncthreads();                    // Ks0 is refilled by iteration 0
-
-    int j = 0;
-    for (; j + 1 < n_tiles; j += 2) {
-        step(B0{}, j, sA, sB);
-        step(B1{}, j + 1, sB, sA);
-    }
-    if (j < n_tiles) step(B0{}, j, sA, sB);
-
-    const int qi = q0w + n;
-    store_row<D, OUT_F32>(o, m_run, l_run, (int64_t)bh * Sq + qi, qi < Sq, qi >= Sq_b, hh, out, lse);
-}
-
-// ---------------------------------------------------------------------------
-// attn_fwd_ws_kernel: V^T tiles prepared in a workspace (v_prep_kernel), both
-// K and V DMAed into LDS.  Sub-iteration j issues three independent streams
+// Main loop: sub-iteration j issues three independent streams
 // of work so that one wave keeps both the MFMA pipe and the VALU busy: the
 // scores of tile j+1 (MFMA), the softmax of tile j (VALU) and
 // O += P_{j-1} V_{j-1} (MFMA).  The body is cut into DT chunks separated by
@@ -437,19 +217,19 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // slice of the softmax and the LDS fragment reads of the next chunk.  The
 // lazy O rescale of tile j is applied after P_{j-1} V_{j-1}.  One barrier
 // per tile; during sub-iteration j the DMAs of K_{j+2} and V_j are in flight.
-template <int D, bool OUT_F32, bool FQ>
-__global__ void __attribute__((amdgpu_flat_work_group_size(WS_WAVES * 64, WS_WAVES * 64)))
+template <int D, bool OUT_F32, bool FQ, bool VPREP>
+__global__ void __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                    const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
                    float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
                    int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
                    const int* __restrict__ lkv) {
-    constexpr int BM = WS_WAVES * QPW;
+    constexpr int BM = WAVES * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int TILE = BN * D;                         // elements of one K or V tile
-    constexpr int KDMA = TILE * 2 / 1024 / WS_WAVES;     // 1 KB DMA chunks per wave per tile
-    static_assert(KDMA >= 1 && KDMA * WS_WAVES * 1024 == TILE * 2, "tile shape");
+    constexpr int KDMA = TILE * 2 / 1024 / WAVES;     // 1 KB DMA chunks per wave per tile
+    static_assert(KDMA >= 1 && KDMA * WAVES * 1024 == TILE * 2, "tile shape");
 
     __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
@@ -568,6 +348,33 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
     };
     // V tile `tile` of this head is the image at vbh + tile*TILE (tile < n_vt).
+    // V through registers (no workspace): thread (kp, dc) of wave w loads
+    // keys 2kp, 2kp+1 at d-chunk dc (8 elements) of tile j at the start of
+    // the iteration and writes them, as fp16 key pairs, into the V^T image
+    // layout at its end.  Lanes vary kp fastest, so one wave's stores of a
+    // given d fill a whole 128-byte image row.
+    constexpr int VDC = D / 8;                        // d-chunks per key row
+    const int v_kp = lane & 31, v_dc = (wave * 64 + lane) >> 5;
+    const bool v_on = VDC * 32 == WAVES * 64 || v_dc < VDC;   // every thread when D = 128
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(v + (int64_t)bkv * kv_bh_stride), (short)0, VPREP ? 0 : Skv * D * 2, RSRC_WORD3);
+    u32x4 vst[2];
+    auto load_v = [&](int kv0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            vst[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((kv0 + 2 * v_kp + i) * D + 8 * v_dc) * 2, 0, 0);
+    };
+    auto store_v = [&](auto b) {
+        if (v_on) {
+            const int col = vt_col(2 * v_kp);         // even: keys 2kp, 2kp+1 stay adjacent
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = 8 * v_dc + e;
+                *(unsigned*)(Vbuf(b) + d * BN + 8 * ((col >> 3) ^ ((d >> 1) & 7)) + (col & 7)) =
+                    pick_pair_f16(vst[0], vst[1], e);
+            }
+        }
+    };
     const uint16_t* vbh = vws + (int64_t)bkv * n_vt * TILE;
     auto dma_v = [&](int tile, auto b) {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -611,7 +418,7 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         const std::integral_constant<int, 1 - decltype(b)::value> nb{};
         const int kv0 = j * BN;
         dma_k(kv0 + 2 * BN, b);        // K_{j+2} -> the buffer K_j used
-        dma_v(j, b);                   // V_j -> the buffer V_{j-2} used
+        if constexpr (VPREP) dma_v(j, b);      // V_j -> the buffer V_{j-2} used
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -658,6 +465,11 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                     w4[kb][u][e] = p_pair(sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1], c, neg_m, lsum);
                 }
             }
+            // Without a workspace, V_j is loaded into registers half-way
+            // through (a short live range) and stored at the end.
+            if constexpr (!VPREP) {
+                if (t == NCH / 2) load_v(kv0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -672,6 +484,7 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                 for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
         }
         if (needs_mask(kv0 + BN)) mask_tile(sn, kv0 + BN, Skv, causal, q0w + n, hh);
+        if constexpr (!VPREP) store_v(b);     // V_j -> the buffer V_{j-2} used
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K_{j+2}, V_j have landed in LDS
         __syncthreads();
     };
@@ -683,8 +496,8 @@ attn_fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     dma_k(0, B0{});
     dma_k(BN, B1{});
 #pragma unroll
-    for (int i = 0; i < TILE / (WS_WAVES * 512); ++i)
-        *(u32x4*)(Vt1 + (i * WS_WAVES * 64 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < TILE / (WAVES * 512); ++i)
+        *(u32x4*)(Vt1 + (i * WAVES * 64 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -733,23 +546,22 @@ template <int D, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
                   int BH, int H, int G, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
                   const QNormRope* qn, const int* lq, const int* lkv, hipStream_t stream) {
-    const int waves = vws ? WS_WAVES : GEN_WAVES;
-    const int BM = waves * QPW;
+    constexpr int BM = WAVES * QPW;
     const int n_qtiles = (Sq + BM - 1) / BM;
     const int64_t nblk = (int64_t)n_qtiles * BH;
     if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const QNormRope qz{};
+    auto go = [&](auto kern, const QNormRope& qa) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(WAVES * 64), 0, stream, (const uint16_t*)q,
+                           (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)vws, kv_bh_stride, out, lse, Sq,
+                           Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, qa, lq, lkv);
+    };
     if (vws && qn)
-        hipLaunchKernelGGL((attn_fwd_ws_kernel<D, OUT_F32, true>), dim3((unsigned)nblk), dim3(WS_WAVES * 64), 0,
-                           stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vws, kv_bh_stride, out,
-                           lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, *qn, lq, lkv);
+        go(attn_fwd_kernel<D, OUT_F32, true, true>, *qn);
     else if (vws)
-        hipLaunchKernelGGL((attn_fwd_ws_kernel<D, OUT_F32, false>), dim3((unsigned)nblk), dim3(WS_WAVES * 64), 0,
-                           stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vws, kv_bh_stride, out,
-                           lse, Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, QNormRope{}, lq, lkv);
+        go(attn_fwd_kernel<D, OUT_F32, false, true>, qz);
     else
-        hipLaunchKernelGGL((attn_fwd_kernel<D, OUT_F32>), dim3((unsigned)nblk), dim3(GEN_WAVES * 64), 0, stream,
-                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, kv_bh_stride, out, lse,
-                           Sq, Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, lq, lkv);
+        go(attn_fwd_kernel<D, OUT_F32, false, false>, qz);
     return hipGetLastError();
 }
 
