@@ -16,6 +16,8 @@ pytestmark = pytest.mark.gpu
     (2, 3, 61, 128, ("video", 1, 1, 61)),
     (1, 1, 1, 128, ("line", 1)),
     (1, 4, 600, 128, ("video", 2, 15, 20)),
+    (3, 29, 37, 64, ("line", 37)),          # 87 (b,h) rows: three groups of 40 heads per thread, the last ragged
+    (2, 41, 19, 128, ("line", 19)),         # 82 rows: a group boundary inside a batch
 ])
 def test_prologue_matches_oracle(B, H, S, D, grid):
     q = inputs.random_bits(S + 1, (B, H, S, D), std=1.5)
