@@ -83,3 +83,28 @@ def test_ws_rejects_small_or_misplaced_workspace():
         attn_fwd_ws(q, q, q, out, out=out[: B * H * S * D].view(B, H, S, D))
     assert e.value.status == 5
     np.testing.assert_equal(n, B * H * (S // 64) * 64 * D * 2)
+
+
+def test_value_range_of_v():
+    """V spanning 2^-20 .. 2^15.9 in magnitude (P V runs on fp16 operands):
+    within [2^-14, 65504] the bf16 -> fp16 conversion is exact, below it the
+    absolute error stays under 2^-25, so the fp32 output tracks the oracle
+    to the fp16 rounding of P, relative to the largest |v|."""
+    B, H, Sq, Skv, D = 1, 2, 200, 300, 128
+    rng = np.random.default_rng(97)
+    mag = np.exp2(rng.uniform(-20.0, 15.9, size=(B, H, Skv, D)))
+    v = inputs.to_bf16_bits(np.where(rng.random(mag.shape) < 0.5, -mag, mag).astype(np.float32))
+    q = inputs.random_bits(98, (B, H, Sq, D))
+    k = inputs.random_bits(99, (B, H, Skv, D))
+    dq, dk, dv = dev_bits(q), dev_bits(k), dev_bits(v)
+    say("[attn_ws] value range of v")
+    o1, l1 = attn_fwd_ws(dq, dk, dv, _ws(B, H, Skv, D), out_dtype=torch.float32)
+    o0, l0 = attn_fwd(dq, dk, dv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+    ref_o, ref_l = oracle.attn(q, k, v, 1 / math.sqrt(D), False)
+    got = host_f64(o1)
+    vmax = float(np.max(np.abs(inputs.bf16_bits_to_f64(v))))
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref_o))) <= 2.0 ** -10 * vmax
+    assert float(np.max(np.abs(host_f64(l1) - ref_l))) <= 1e-3
