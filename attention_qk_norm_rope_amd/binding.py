@@ -51,12 +51,13 @@ def _load():
     lib.attn_fwd_workspace_bytes.restype = i64
     lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
                                         i32, p]
+    lib.attn_fwd_ws_bsnd.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
     lib.attn_fwd_varlen.argtypes = [p, p, p, p, i64, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_fwd_ws_fused_q",
-                 "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd"):
+                 "attn_fwd_ws_bsnd", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -155,7 +156,7 @@ def _kv_bh_stride(t, B, H, S, D) -> int | None:
     return s1
 
 
-def _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse, kv_heads=None):
+def _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse, kv_heads=None, bsnd_out=False):
     _need(q, "q", torch.bfloat16, q.device)
     dev = q.device
     _need(k, "k", torch.bfloat16, dev)
@@ -173,7 +174,13 @@ def _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse, kv_heads=None):
         raise ValueError("k and v must be [B,H,Skv,D] with contiguous rows and the same (b,h) stride")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
+    if bsnd_out:
+        if (not isinstance(out, torch.Tensor) or out.dim() != 4 or out.shape[0] != B or out.shape[1] != Sq
+                or out.shape[3] != D or not out.is_contiguous()):
+            raise ValueError(f"out must be a contiguous BSND tensor [{B},{Sq},heads,{D}]")
+        if out.device != dev:
+            raise ValueError("out is on another device")
+    elif out is None:
         out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=dev)
     else:
         if tuple(out.shape) != (B, H, Sq, D) or not out.is_contiguous():
@@ -309,6 +316,24 @@ def attn_fwd_ws_fused_q(q, k, v, workspace, w_q, cos_q, sin_q, eps: float, out=N
                                      _ptr(w_q), _ptr(cos_q), _ptr(sin_q), float(eps), B, H, Sq, Skv, D, scale,
                                      1 if causal else 0, _dtype_code(out), _stream())
     _check("attn_fwd_ws_fused_q", st)
+    return out, lse
+
+
+def attn_fwd_ws_bsnd(q, k, v, workspace, out, out_h0: int = 0, lse=None, scale: float | None = None,
+                     causal: bool = False, return_lse: bool = True):
+    """attn_fwd_ws whose epilogue stores into the model's BSND layout: out is
+    a contiguous bf16 or fp32 tensor [B, Sq, heads, D]; query head h writes
+    out[:, :, out_h0 + h, :] and the other heads are left as they are.
+    lse stays fp32 [B,H,Sq].  Returns (out, lse)."""
+    (B, H, Sq, Skv, D), sk, scale, out, lse = _attn_args(q, k, v, out, lse, scale, None, return_lse,
+                                                         bsnd_out=True)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _load().attn_fwd_ws_bsnd(_ptr(q), _ptr(k), _ptr(v), sk, _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                                  B, H, Sq, Skv, D, scale, 1 if causal else 0, _dtype_code(out),
+                                  int(out.shape[2]), int(out_h0), _stream())
+    _check("attn_fwd_ws_bsnd", st)
     return out, lse
 
 

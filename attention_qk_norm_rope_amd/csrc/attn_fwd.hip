@@ -178,12 +178,12 @@ __device__ __forceinline__ unsigned p_pair(float s0, float s1, float c, float ne
     return pk;
 }
 
-// O /= l, store the row (bf16 or fp32) and LSE = ln2 * (m + log2 l).
-// A padding row (pad) and a row that saw no key (l = 0) store zeros and
-// LSE = -inf.
+// O /= l, store the row (bf16 or fp32) at out + orow*D and LSE[lrow] =
+// ln2 * (m + log2 l).  A padding row (pad) and a row that saw no key (l = 0)
+// store zeros and LSE = -inf.
 template <int D, bool OUT_F32>
-__device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run, float l_half, int64_t row,
-                                          bool valid, bool pad, int hh, void* out, float* lse) {
+__device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run, float l_half, int64_t orow,
+                                          int64_t lrow, bool valid, bool pad, int hh, void* out, float* lse) {
     const float l = pair_sum(l_half);
     const bool empty = pad || !(l > 0.f);
     const float inv = empty ? 0.f : 1.0f / l;
@@ -198,14 +198,14 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run
             if (empty) a0 = a1 = a2 = a3 = 0.f;   // not 0 * (garbage of padding rows)
             if constexpr (OUT_F32) {
                 f32x4 w = {a0, a1, a2, a3};
-                *(f32x4*)((float*)out + row * D + d) = w;
+                *(f32x4*)((float*)out + orow * D + d) = w;
             } else {
                 u32x2 w = {pack_bf16(a0, a1), pack_bf16(a2, a3)};
-                *(u32x2*)((uint16_t*)out + row * D + d) = w;
+                *(u32x2*)((uint16_t*)out + orow * D + d) = w;
             }
         }
     // v_log_f32 is log2.
-    if (lse && hh == 0) lse[row] = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l)) * LN2;
+    if (lse && hh == 0) lse[lrow] = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l)) * LN2;
 }
 
 // ---------------------------------------------------------------------------
@@ -224,7 +224,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
                    const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
                    float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
                    int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
-                   const int* __restrict__ lkv) {
+                   const int* __restrict__ lkv, int out_heads, int out_h0) {
     constexpr int BM = WAVES * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int TILE = BN * D;                         // elements of one K or V tile
@@ -538,14 +538,18 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
         last_pv(B1{}, pB);
     }
 
+    // Output row: BNSD [B,H,Sq,D], or head out_h0 + h of a BSND [B,Sq,out_heads,D] tensor.
     const int qi = q0w + n;
-    store_row<D, OUT_F32>(o, m_run, l_run, (int64_t)bh * Sq + qi, qi < Sq, qi >= Sq_b, hh, out, lse);
+    const int64_t lrow = (int64_t)bh * Sq + qi;
+    const int64_t orow = out_heads ? ((int64_t)(bh / H) * Sq + qi) * out_heads + out_h0 + bh % H : lrow;
+    store_row<D, OUT_F32>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse);
 }
 
 template <int D, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
                   int BH, int H, int G, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
-                  const QNormRope* qn, const int* lq, const int* lkv, hipStream_t stream) {
+                  const QNormRope* qn, const int* lq, const int* lkv, int out_heads, int out_h0,
+                  hipStream_t stream) {
     constexpr int BM = WAVES * QPW;
     const int n_qtiles = (Sq + BM - 1) / BM;
     const int64_t nblk = (int64_t)n_qtiles * BH;
@@ -554,7 +558,7 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
     auto go = [&](auto kern, const QNormRope& qa) {
         hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(WAVES * 64), 0, stream, (const uint16_t*)q,
                            (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)vws, kv_bh_stride, out, lse, Sq,
-                           Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, qa, lq, lkv);
+                           Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, qa, lq, lkv, out_heads, out_h0);
     };
     if (vws && qn)
         go(attn_fwd_kernel<D, OUT_F32, true, true>, *qn);
@@ -570,7 +574,7 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
                            bool causal, bool out_f32, const void* vws, const QNormRope* qn, const int* lq,
-                           const int* lkv, hipStream_t stream) {
+                           const int* lkv, int out_heads, int out_h0, hipStream_t stream) {
     // Positive multiplier for exp2; the sign of the scale goes into Q.  A
     // zero (or vanishing) scale keeps a tiny positive multiplier so that
     // masked logits (-inf) still map to probability 0; the logits it yields
@@ -579,10 +583,10 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
     if (!(c >= 1e-30f)) c = 1e-30f;
     const unsigned qsign = scale < 0.f ? 0x80008000u : 0u;
     if (D == 128)
-        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, stream)
-                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, stream);
-    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, stream)
-                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, stream);
+        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, stream)
+                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, stream);
+    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, stream)
+                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, stream);
 }
 
 }  // namespace dit

@@ -63,13 +63,15 @@ int qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k, const flo
 namespace {
 
 // Shared argument checks of the attention entry points; on success fills
-// the byte ranges of every tensor for the alias checks.
+// the byte ranges of every tensor for the alias checks.  out_heads > 0 means
+// out is BSND [B, Sq, out_heads, D] receiving heads [out_h0, out_h0 + H).
 struct AttnRanges {
     Range q, k, v, out, lse;
 };
 
 int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
-               int B, int H, int Hkv, int Sq, int Skv, int D, float scale, int out_dtype, AttnRanges* r) {
+               int B, int H, int Hkv, int Sq, int Skv, int D, float scale, int out_dtype, AttnRanges* r,
+               int out_heads = 0, int out_h0 = 0) {
     if (!q || !k || !v || !out) return DIT_ERR_NULL;
     if (B < 1 || H < 1 || Sq < 1 || Skv < 1 || D < 1) return DIT_ERR_SHAPE;
     if (Hkv < 1 || Hkv > H || H % Hkv != 0) return DIT_ERR_SHAPE;
@@ -79,6 +81,10 @@ int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride
     const int64_t BH = (int64_t)B * H;
     const int64_t q_elems = BH * Sq * D;
     if (BH > 0x7FFFFFFF || q_elems > kMaxElems) return DIT_ERR_SHAPE;
+    if (out_heads < 0 || (out_heads > 0 && (out_heads < H || out_h0 < 0 || out_h0 > out_heads - H)))
+        return DIT_ERR_SHAPE;
+    const int64_t out_elems = out_heads > 0 ? (int64_t)B * Sq * out_heads * D : q_elems;
+    if (out_elems > kMaxElems) return DIT_ERR_SHAPE;
     // The kernel addresses one (b,h) slab of q/k/v with 32-bit buffer offsets
     // (including up to three tiles of read-ahead past the end).
     if ((int64_t)(Sq + 512) * D * 2 > 0x7FFFFFFF || (int64_t)(Skv + 512) * D * 2 > 0x7FFFFFFF)
@@ -93,7 +99,7 @@ int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride
     r->q = range_of(q, q_elems * 2);
     r->k = range_of(k, kv_elems * 2);
     r->v = range_of(v, kv_elems * 2);
-    r->out = range_of(out, q_elems * (out_dtype == DIT_FP32 ? 4 : 2));
+    r->out = range_of(out, out_elems * (out_dtype == DIT_FP32 ? 4 : 2));
     r->lse = range_of(lse, lse ? BH * Sq * 4 : 0);
     if (overlap(r->out, r->q) || overlap(r->out, r->k) || overlap(r->out, r->v)) return DIT_ERR_ALIAS;
     if (lse && (overlap(r->lse, r->q) || overlap(r->lse, r->k) || overlap(r->lse, r->v) || overlap(r->lse, r->out)))
@@ -106,9 +112,10 @@ int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride
 int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
                 int64_t workspace_bytes, void* out, float* lse, int B, int H, int Hkv, int Sq, int Skv, int D,
                 float scale, int causal, int out_dtype, const dit::QNormRope* qn, const int* lq, const int* lkv,
-                hipStream_t stream) {
+                hipStream_t stream, int out_heads = 0, int out_h0 = 0) {
     AttnRanges r;
-    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Hkv, Sq, Skv, D, scale, out_dtype, &r);
+    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Hkv, Sq, Skv, D, scale, out_dtype, &r,
+                              out_heads, out_h0);
     if (st != DIT_OK) return st;
     if (workspace) {
         if (!aligned(workspace, 16)) return DIT_ERR_ALIGN;
@@ -142,7 +149,8 @@ int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_strid
         if (e != hipSuccess) return DIT_ERR_HIP;
     }
     return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, H, H / Hkv, Sq, Skv, D, scale,
-                                           causal != 0, out_dtype == DIT_FP32, workspace, qn, lq, lkv, stream));
+                                           causal != 0, out_dtype == DIT_FP32, workspace, qn, lq, lkv, out_heads,
+                                           out_h0, stream));
 }
 
 // Shared checks of the layout entry points: a is the BSND tensor, b the BNSD slice.
@@ -210,6 +218,20 @@ int attn_fwd_ws_fused_q(const void* q, const void* k, const void* v, int64_t kv_
     const dit::QNormRope qn{w_q, cos_q, sin_q, eps};
     return attn_common(q, k, v, kv_bh_stride, workspace, workspace_bytes, out, lse, B, H, H, Sq, Skv, D, scale,
                        causal, out_dtype, &qn, nullptr, nullptr, stream);
+}
+
+int attn_fwd_ws_bsnd(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
+                     int64_t workspace_bytes, void* out, float* lse, int B, int H, int Sq, int Skv, int D,
+                     float scale, int causal, int out_dtype, int out_heads, int out_h0, hipStream_t stream) {
+    if (!workspace) {
+        AttnRanges r;
+        const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, H, Sq, Skv, D, scale, out_dtype, &r,
+                                  out_heads, out_h0);
+        return st != DIT_OK ? st : DIT_ERR_NULL;
+    }
+    if (out_heads < 1) return DIT_ERR_SHAPE;
+    return attn_common(q, k, v, kv_bh_stride, workspace, workspace_bytes, out, lse, B, H, H, Sq, Skv, D, scale,
+                       causal, out_dtype, nullptr, nullptr, nullptr, stream, out_heads, out_h0);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* workspace, int64_t workspace_bytes,

@@ -105,9 +105,12 @@ def traffic_entry(kernel: str, workload: str):
 
 def bench_ulysses(args):
     """bsnd_to_bnsd + bnsd_to_bsnd of one rank's 10 heads (4-way split) of
-    B1 S75600 H40 D128 bf16: 2 bytes read + 2 written per element each way."""
+    B1 S75600 H40 D128 bf16: 2 bytes read + 2 written per element each way.
+    Then that rank's attention (10 heads, 75600 keys) stored back into BSND,
+    once as attn_fwd_ws + bnsd_to_bsnd and once as attn_fwd_ws_bsnd."""
     import torch
-    from attention_qk_norm_rope_amd import bnsd_to_bsnd, bsnd_to_bnsd
+    from attention_qk_norm_rope_amd import (attn_fwd_workspace_bytes, attn_fwd_ws, attn_fwd_ws_bsnd, bnsd_to_bsnd,
+                                            bsnd_to_bnsd)
     B, S, H, D, P = 1, 75600, 40, 128, 4
     hs = H // P
     dev = torch.device("cuda:0")
@@ -134,6 +137,39 @@ def bench_ulysses(args):
     t_pre = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     t_post = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     gbs = lambda t: round(nbytes / (t * 1e-3) / 1e9, 1)  # noqa: E731
+
+    # The rank's attention with its output returned to BSND, two ways.
+    q = bsnd_to_bnsd(x, 0, hs)
+    k = bsnd_to_bnsd(x, hs, hs)
+    v = bsnd_to_bnsd(x, 2 * hs, hs)
+    ws = torch.empty((attn_fwd_workspace_bytes(B, hs, S, D),), dtype=torch.uint8, device=dev)
+    ob = torch.empty((B, hs, S, D), dtype=torch.bfloat16, device=dev)
+
+    def two_pass():
+        attn_fwd_ws(q, k, v, ws, out=ob)
+        bnsd_to_bsnd(ob, y, 0)
+
+    def fused():
+        attn_fwd_ws_bsnd(q, k, v, ws, y, out_h0=0)
+
+    att = {}
+    n_att = max(1, min(args.steps, 3))
+    for name, fn in (("attn_fwd_ws+bnsd_to_bsnd", two_pass), ("attn_fwd_ws_bsnd", fused)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n_att):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        att[name] = round(a.elapsed_time(b) / n_att, 3)
+    y2 = torch.empty_like(y)
+    attn_fwd_ws(q, k, v, ws, out=ob)
+    bnsd_to_bsnd(ob, y2, 0)
+    attn_fwd_ws_bsnd(q, k, v, ws, y, out_h0=0)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y[:, :, :hs], y2[:, :, :hs]))
     print(json.dumps({
         "metric": "Ulysses head-slice layout GB/s (auxiliary measurement, not the headline metric)",
         "value": gbs((t_pre + t_post) / 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -144,6 +180,7 @@ def bench_ulysses(args):
                                      "frac_hbm_peak": round(nbytes / (t_pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
                     "bnsd_to_bsnd": {"avg_ms": round(t_post, 4), "bytes": nbytes, "gbs": gbs(t_post),
                                      "frac_hbm_peak": round(nbytes / (t_post * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}},
+        "attention_to_bsnd_ms": att, "attention_to_bsnd_same_bits": same,
     }), flush=True)
 
 

@@ -7,6 +7,7 @@
  *   attn_fwd_gqa   the same with Hkv K/V heads shared by H query heads
  *   attn_fwd_varlen  the same over padded batches with per-batch lengths
  *   attn_fwd_ws_fused_q  attention with the query prologue fused into its Q load
+ *   attn_fwd_ws_bsnd  attention storing its output into a head slice of a BSND tensor
  *   attn_merge     fold of two partial attentions over disjoint key sets
  *   bsnd_to_bnsd, bnsd_to_bsnd  head-slice layout change of Ulysses sequence parallelism
  *
@@ -211,6 +212,28 @@ int attn_fwd_ws_fused_q(const void *q, const void *k, const void *v, int64_t kv_
                         const float *w_q, const float *cos_q, const float *sin_q, float eps,
                         int B, int H, int Sq, int Skv, int D, float scale, int causal,
                         int out_dtype, hipStream_t stream);
+
+/*
+ * attn_fwd_ws with the output stored in the model's BSND layout.
+ * [WAN] npu_fused_infer_attention_score returns BNSD and the caller
+ * transposes it back to [B,S,N,D]. [PR274] item 2 (npu_ulysses_attention)
+ * does the same before its all-to-all. Here the attention epilogue writes
+ * each row straight to its BSND place:
+ *   out[b, i, out_h0 + h, :] = attention row (b, h, i)
+ * The other heads of out are not touched. lse stays fp32 [B,H,Sq].
+ *
+ *   out        [B, Sq, out_heads, D] of out_dtype
+ *   out_heads  >= H; out_h0 satisfies 0 <= out_h0 <= out_heads - H
+ *
+ * The bits are those of attn_fwd_ws followed by bnsd_to_bsnd (for bf16 out).
+ * DIT_ERR_SHAPE for a bad out_heads or out_h0. out must not overlap q, k, v,
+ * lse or the workspace over its whole BSND extent. All other arguments and
+ * errors are as for attn_fwd_ws.
+ */
+int attn_fwd_ws_bsnd(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
+                     void *workspace, int64_t workspace_bytes, void *out, float *lse,
+                     int B, int H, int Sq, int Skv, int D, float scale, int causal,
+                     int out_dtype, int out_heads, int out_h0, hipStream_t stream);
 
 /*
  * Merge of two partial attentions over disjoint key sets, in place into

@@ -47,6 +47,7 @@ def lib():
     lib.attn_fwd_gqa.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
                                         i32, p]
+    lib.attn_fwd_ws_bsnd.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
     lib.attn_fwd_varlen.argtypes = [p, p, p, p, i64, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
@@ -59,7 +60,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
-                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd",
+                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd",
                           "bnsd_to_bsnd", "dit_attn_status_string",
                           "dit_attn_version"}, names
     for name in names:
@@ -182,6 +183,27 @@ def test_attn_fwd_ws_fused_q_rejections(lib):
     assert call(cq=O) == ALIAS                           # a table on the output
     assert call(sq=WS) == ALIAS                          # a table on the workspace
     assert call(o=None) == NULL
+
+
+def test_attn_fwd_ws_bsnd_rejections(lib):
+    f = lib.attn_fwd_ws_bsnd
+    need = 2 * 4 * 64 * 64 * 2
+    # B1, H2, Sq = Skv = 256, D64 into a BSND output of `heads` heads.
+
+    def call(heads=6, h0=2, ws=WS, o=O, dt=BF16, lse=L):
+        return f(Q, K, V, 256 * 64, ws, need, o, lse, 1, 2, 256, 256, 64, 0.125, 0, dt, heads, h0, None)
+
+    assert call(ws=None) == NULL
+    assert call(o=None) == NULL
+    assert call(heads=0) == SHAPE
+    assert call(heads=1) == SHAPE                        # fewer output heads than query heads
+    assert call(h0=-1) == SHAPE
+    assert call(h0=5) == SHAPE                           # heads 5, 6 do not exist
+    assert call(heads=2, h0=0, o=O + 8) == ALIGN
+    out_bytes = 256 * 6 * 64 * 2
+    assert call(lse=O + out_bytes - 1024) == ALIAS       # lse inside the BSND extent
+    assert call(ws=O + out_bytes - need + 16) == ALIAS   # workspace runs into out
+    assert call(dt=FP32, ws=O + out_bytes) == ALIAS      # fp32 out is twice as long
 
 
 def test_qk_norm_rope_rejections(lib):
