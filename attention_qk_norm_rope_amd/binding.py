@@ -52,12 +52,13 @@ def _load():
     lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
                                         i32, p]
     lib.attn_fwd_ws_bsnd.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, p]
+    lib.attn_fwd_ws_merge.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
     lib.attn_fwd_varlen.argtypes = [p, p, p, p, i64, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_fwd_ws_fused_q",
-                 "attn_fwd_ws_bsnd", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd"):
+                 "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -335,6 +336,24 @@ def attn_fwd_ws_bsnd(q, k, v, workspace, out, out_h0: int = 0, lse=None, scale: 
                                   int(out.shape[2]), int(out_h0), _stream())
     _check("attn_fwd_ws_bsnd", st)
     return out, lse
+
+
+def attn_fwd_ws_merge(q, k, v, workspace, out_a, lse_a, scale: float | None = None, causal: bool = False):
+    """Attention of q over (k, v) merged in place into the running partial
+    result (out_a bf16/fp32 [B,H,Sq,D], lse_a fp32 [B,H,Sq]) of the same
+    queries over other keys.  Same bits as attn_fwd_ws into an fp32
+    temporary followed by attn_merge.  Returns (out_a, lse_a)."""
+    if lse_a is None:
+        raise ValueError("lse_a is required")
+    (B, H, Sq, Skv, D), sk, scale, out_a, lse_a = _attn_args(q, k, v, out_a, lse_a, scale, None, True)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _load().attn_fwd_ws_merge(_ptr(q), _ptr(k), _ptr(v), sk, _ptr(workspace), ws_bytes, _ptr(out_a),
+                                   _ptr(lse_a), B, H, Sq, Skv, D, scale, 1 if causal else 0, _dtype_code(out_a),
+                                   _stream())
+    _check("attn_fwd_ws_merge", st)
+    return out_a, lse_a
 
 
 def attn_merge(out_a, lse_a, out_b, lse_b):

@@ -51,6 +51,7 @@
 //    over 8 XCDs) works on a contiguous range of (b,h, q-tile): the query
 //    tiles of one head share that head's K/V through one XCD's L2.
 #include "internal.h"
+#include "merge_math.h"
 #include "norm_rope.h"
 
 #include <math.h>
@@ -180,32 +181,54 @@ __device__ __forceinline__ unsigned p_pair(float s0, float s1, float c, float ne
 
 // O /= l, store the row (bf16 or fp32) at out + orow*D and LSE[lrow] =
 // ln2 * (m + log2 l).  A padding row (pad) and a row that saw no key (l = 0)
-// store zeros and LSE = -inf.
-template <int D, bool OUT_F32>
+// store zeros and LSE = -inf.  MERGE: out/lse already hold a partial
+// attention of the same row over other keys; the row is folded into it with
+// the arithmetic of attn_merge (this side in fp32, as an fp32 out_b).
+template <int D, bool OUT_F32, bool MERGE>
 __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run, float l_half, int64_t orow,
                                           int64_t lrow, bool valid, bool pad, int hh, void* out, float* lse) {
     const float l = pair_sum(l_half);
     const bool empty = pad || !(l > 0.f);
     const float inv = empty ? 0.f : 1.0f / l;
     if (!valid) return;
+    // v_log_f32 is log2.
+    const float lb = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l)) * LN2;
+    float wa = 0.f, wb = 0.f, lm = lb;
+    if constexpr (MERGE) mg::weights(lse[lrow], lb, wa, wb, lm);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d = 32 * db + 8 * g + 4 * hh;
-            float a0 = o[db][4 * g + 0] * inv, a1 = o[db][4 * g + 1] * inv;
-            float a2 = o[db][4 * g + 2] * inv, a3 = o[db][4 * g + 3] * inv;
-            if (empty) a0 = a1 = a2 = a3 = 0.f;   // not 0 * (garbage of padding rows)
+            float a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = empty ? 0.f : o[db][4 * g + i] * inv;   // not 0 * garbage
+            if constexpr (MERGE) {
+                float x[4];
+                if constexpr (OUT_F32) {
+                    const f32x4 r = *(const f32x4*)((const float*)out + orow * D + d);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = r[i];
+                } else {
+                    const u32x2 r = *(const u32x2*)((const uint16_t*)out + orow * D + d);
+                    x[0] = __builtin_bit_cast(float, r[0] << 16);
+                    x[1] = __builtin_bit_cast(float, r[0] & 0xFFFF0000u);
+                    x[2] = __builtin_bit_cast(float, r[1] << 16);
+                    x[3] = __builtin_bit_cast(float, r[1] & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = mg::combine(wa, x[i], wb, a[i]);
+            }
             if constexpr (OUT_F32) {
-                f32x4 w = {a0, a1, a2, a3};
+                f32x4 w = {a[0], a[1], a[2], a[3]};
                 *(f32x4*)((float*)out + orow * D + d) = w;
             } else {
-                u32x2 w = {pack_bf16(a0, a1), pack_bf16(a2, a3)};
+                u32x2 w = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])};
                 *(u32x2*)((uint16_t*)out + orow * D + d) = w;
             }
         }
-    // v_log_f32 is log2.
-    if (lse && hh == 0) lse[lrow] = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l)) * LN2;
+    // Both lanes of the row read lse[lrow] above (same wave, in order).
+    if (lse && hh == 0) lse[lrow] = lm;
 }
 
 // ---------------------------------------------------------------------------
@@ -217,7 +240,7 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run
 // slice of the softmax and the LDS fragment reads of the next chunk.  The
 // lazy O rescale of tile j is applied after P_{j-1} V_{j-1}.  One barrier
 // per tile; during sub-iteration j the DMAs of K_{j+2} and V_j are in flight.
-template <int D, bool OUT_F32, bool FQ, bool VPREP>
+template <int D, bool OUT_F32, bool FQ, bool VPREP, bool MERGE = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -542,13 +565,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     const int qi = q0w + n;
     const int64_t lrow = (int64_t)bh * Sq + qi;
     const int64_t orow = out_heads ? ((int64_t)(bh / H) * Sq + qi) * out_heads + out_h0 + bh % H : lrow;
-    store_row<D, OUT_F32>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse);
+    store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse);
 }
 
 template <int D, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
                   int BH, int H, int G, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
-                  const QNormRope* qn, const int* lq, const int* lkv, int out_heads, int out_h0,
+                  const QNormRope* qn, const int* lq, const int* lkv, int out_heads, int out_h0, bool merge,
                   hipStream_t stream) {
     constexpr int BM = WAVES * QPW;
     const int n_qtiles = (Sq + BM - 1) / BM;
@@ -560,7 +583,9 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
                            (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)vws, kv_bh_stride, out, lse, Sq,
                            Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, qa, lq, lkv, out_heads, out_h0);
     };
-    if (vws && qn)
+    if (merge)
+        go(attn_fwd_kernel<D, OUT_F32, false, true, true>, qz);
+    else if (vws && qn)
         go(attn_fwd_kernel<D, OUT_F32, true, true>, *qn);
     else if (vws)
         go(attn_fwd_kernel<D, OUT_F32, false, true>, qz);
@@ -574,7 +599,7 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
                            bool causal, bool out_f32, const void* vws, const QNormRope* qn, const int* lq,
-                           const int* lkv, int out_heads, int out_h0, hipStream_t stream) {
+                           const int* lkv, int out_heads, int out_h0, bool merge, hipStream_t stream) {
     // Positive multiplier for exp2; the sign of the scale goes into Q.  A
     // zero (or vanishing) scale keeps a tiny positive multiplier so that
     // masked logits (-inf) still map to probability 0; the logits it yields
@@ -583,10 +608,10 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
     if (!(c >= 1e-30f)) c = 1e-30f;
     const unsigned qsign = scale < 0.f ? 0x80008000u : 0u;
     if (D == 128)
-        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, stream)
-                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, stream);
-    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, stream)
-                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, stream);
+        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, merge, stream)
+                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, merge, stream);
+    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, merge, stream)
+                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, merge, stream);
 }
 
 }  // namespace dit

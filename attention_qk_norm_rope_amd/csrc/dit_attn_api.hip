@@ -112,7 +112,7 @@ int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride
 int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
                 int64_t workspace_bytes, void* out, float* lse, int B, int H, int Hkv, int Sq, int Skv, int D,
                 float scale, int causal, int out_dtype, const dit::QNormRope* qn, const int* lq, const int* lkv,
-                hipStream_t stream, int out_heads = 0, int out_h0 = 0) {
+                hipStream_t stream, int out_heads = 0, int out_h0 = 0, bool merge = false) {
     AttnRanges r;
     const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Hkv, Sq, Skv, D, scale, out_dtype, &r,
                               out_heads, out_h0);
@@ -150,7 +150,7 @@ int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_strid
     }
     return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, H, H / Hkv, Sq, Skv, D, scale,
                                            causal != 0, out_dtype == DIT_FP32, workspace, qn, lq, lkv, out_heads,
-                                           out_h0, stream));
+                                           out_h0, merge, stream));
 }
 
 // Shared checks of the layout entry points: a is the BSND tensor, b the BNSD slice.
@@ -232,6 +232,18 @@ int attn_fwd_ws_bsnd(const void* q, const void* k, const void* v, int64_t kv_bh_
     if (out_heads < 1) return DIT_ERR_SHAPE;
     return attn_common(q, k, v, kv_bh_stride, workspace, workspace_bytes, out, lse, B, H, H, Sq, Skv, D, scale,
                        causal, out_dtype, nullptr, nullptr, nullptr, stream, out_heads, out_h0);
+}
+
+int attn_fwd_ws_merge(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
+                      int64_t workspace_bytes, void* out_a, float* lse_a, int B, int H, int Sq, int Skv, int D,
+                      float scale, int causal, int a_dtype, hipStream_t stream) {
+    if (!workspace || !lse_a) {
+        AttnRanges r;
+        const int st = check_attn(q, k, v, kv_bh_stride, out_a, lse_a, B, H, H, Sq, Skv, D, scale, a_dtype, &r);
+        return st != DIT_OK ? st : DIT_ERR_NULL;
+    }
+    return attn_common(q, k, v, kv_bh_stride, workspace, workspace_bytes, out_a, lse_a, B, H, H, Sq, Skv, D, scale,
+                       causal, a_dtype, nullptr, nullptr, nullptr, stream, 0, 0, true);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* workspace, int64_t workspace_bytes,

@@ -18,6 +18,9 @@ namespace dit {
 // as it loads them (same bits as running qk_norm_rope on q first).
 // With out_heads > 0, out is BSND [B, Sq, out_heads, D] and query head h of
 // batch b writes head out_h0 + h; otherwise out is BNSD [BH, Sq, D].
+// With merge (workspace path, no fused Q), out and lse hold a partial
+// attention over other keys and each row is merged into them as attn_merge
+// would merge an fp32 out_b.
 struct QNormRope {
     const float* w;      // [D]
     const float* cos_t;  // [Sq, D]
@@ -27,7 +30,7 @@ struct QNormRope {
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
                            bool causal, bool out_f32, const void* vws, const QNormRope* qn, const int* lq,
-                           const int* lkv, int out_heads, int out_h0, hipStream_t stream);
+                           const int* lkv, int out_heads, int out_h0, bool merge, hipStream_t stream);
 
 // Bytes of prepared V for BH heads of Skv keys; launch_v_prep writes them.
 int64_t v_prep_bytes(int64_t BH, int Skv, int D);

@@ -11,6 +11,7 @@
 // Layout: D/8 consecutive lanes own one row, 8 elements each (16-byte bf16
 // or 32-byte fp32 accesses).  fp32 arithmetic, one rounding when out_a is bf16.
 #include "internal.h"
+#include "merge_math.h"
 
 #include <math.h>
 
@@ -52,29 +53,15 @@ attn_merge_kernel(void* __restrict__ out_a, float* __restrict__ lse_a, const voi
     constexpr int RPB = 256 / L;
     const int d0 = 8 * (threadIdx.x % L);
     for (int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / L; r < rows; r += (int64_t)gridDim.x * RPB) {
-        const float la = lse_a[r], lb = lse_b[r];
-        const float M = fmaxf(la, lb);
-        float wa = 0.f, wb = 0.f, Lr = -INFINITY;
-        if (M != -INFINITY) {
-            const float ea = expf(la - M), eb = expf(lb - M);
-            const float den = ea + eb;
-            Lr = M + logf(den);
-            wa = ea / den;
-            wb = eb / den;
-        }
+        float wa, wb, Lr;
+        mg::weights(lse_a[r], lse_b[r], wa, wb, Lr);
         const int64_t off = r * D + d0;
         float a[8], b[8];
         load8<AF32>(out_a, off, a);
         load8<BF32>(out_b, off, b);
         float o[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            // A side with weight 0 saw no key: its values are not read into
-            // the result (they may be anything, even NaN).
-            const float ta = wa != 0.f ? wa * a[i] : 0.f;
-            const float tb = wb != 0.f ? wb * b[i] : 0.f;
-            o[i] = ta + tb;
-        }
+        for (int i = 0; i < 8; ++i) o[i] = mg::combine(wa, a[i], wb, b[i]);
         if constexpr (AF32) {
             f32x4 x0 = {o[0], o[1], o[2], o[3]}, x1 = {o[4], o[5], o[6], o[7]};
             *(f32x4*)((float*)out_a + off) = x0;

@@ -10,11 +10,12 @@ as the Ring Attention Overlap of the Wan2.2 NPU page on one GPU:
   1. restore q, k from pristine device copies (the prologue works in place),
   2. qk_norm_rope(q, k): per-head RMSNorm (eps 1e-5) + 3D interleaved RoPE,
   3. attn_fwd_ws over the local quarter of the keys   -> fp32 out_a, lse_a,
-  4. attn_fwd_ws over the remaining three quarters (a window of the same K/V)
-                                                      -> fp32 out_b, lse_b,
-  5. attn_merge(out_a, lse_a, out_b, lse_b).
+  4. attn_fwd_ws_merge over the remaining three quarters (a window of the
+     same K/V), whose epilogue merges each row into (out_a, lse_a) with the
+     arithmetic of attn_merge (--separate-merge: attn_fwd_ws into fp32
+     out_b, lse_b, then attn_merge(out_a, lse_a, out_b, lse_b); same bits).
 Steps 3+4 cover every key once, so the attention work is exactly that of
-full attention: 4*B*H*Sq*Skv*D FLOP per step.  Each attn_fwd_ws call is two
+full attention: 4*B*H*Sq*Skv*D FLOP per step.  Each attention call is two
 kernels, the V rewrite into the workspace and the attention kernel; both sit
 inside the timed interval of the call.
 
@@ -61,13 +62,20 @@ def parse():
     ap.add_argument("--fuse-q", action="store_true",
                     help="wan workload: apply the query RMSNorm+RoPE inside the attention's Q load "
                          "(attn_fwd_ws_fused_q); the prologue kernel then normalises k only")
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="wan workload: the remote attention call writes its own fp32 output and a separate "
+                         "attn_merge kernel folds it into the local one (default: attn_fwd_ws_merge merges in "
+                         "the attention epilogue)")
     ap.add_argument("--ring-streams", type=int, default=1, choices=[1, 2],
                     help="wan workload: run the local and remote attention calls on one stream in order (1) "
                          "or concurrently on two streams (2)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain device copies of a known size (the reference for rocprofv3's "
                          "FETCH_SIZE/WRITE_SIZE counters) and print their byte counts")
-    return ap.parse_args()
+    args = ap.parse_args()
+    # The merging epilogue has no fused-Q variant: --fuse-q keeps the separate merge.
+    args.fuse_merge = not (args.separate_merge or args.fuse_q)
+    return args
 
 
 def calibrate_copy():
@@ -205,7 +213,8 @@ def main():
     import torch
 
     from attention_qk_norm_rope_amd import (attn_fwd_ring_overlap, attn_fwd_workspace_bytes, attn_fwd_ws,
-                                            attn_fwd_ws_fused_q, attn_merge, inputs, qk_norm_rope)
+                                            attn_fwd_ws_fused_q, attn_fwd_ws_merge, attn_merge, inputs,
+                                            qk_norm_rope)
     from attention_qk_norm_rope_amd import binding
 
     if not torch.cuda.is_available():
@@ -270,57 +279,51 @@ def main():
 
         final_out, final_lse = out_a, lse_a
         n_merge = 0
-    elif wl == "wan" and args.fuse_q:
-        c = S // 4
-        out_a = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
-        out_b = torch.empty_like(out_a)
-        lse_a = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
-        lse_b = torch.empty_like(lse_a)
-        names = ["qk_norm_rope", "attn_fwd", "attn_fwd", "attn_merge"]
-
-        def step(ev):
-            k.copy_(k0)
-            ev[0].record()
-            qk_norm_rope(None, k, None, w_k, cos_d, sin_d, cfg.eps)
-            ev[1].record()
-            attn_fwd_ws_fused_q(q0, k[:, :, :c], v[:, :, :c], ws, w_q, cos_d, sin_d, cfg.eps, out=out_a, lse=lse_a,
-                                scale=scale)
-            ev[2].record()
-            attn_fwd_ws_fused_q(q0, k[:, :, c:], v[:, :, c:], ws, w_q, cos_d, sin_d, cfg.eps, out=out_b, lse=lse_b,
-                                scale=scale)
-            ev[3].record()
-            attn_merge(out_a, lse_a, out_b, lse_b)
-            ev[4].record()
-
-        final_out, final_lse = out_a, lse_a
-        merge_rows = B * H * Sq
-        merge_bytes = merge_rows * (D * (4 + 4 + 4) + 12)
-        n_merge = 1
     elif wl == "wan":
         c = S // 4
         out_a = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
         out_b = torch.empty_like(out_a)
         lse_a = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
         lse_b = torch.empty_like(lse_a)
-        names = ["qk_norm_rope", "attn_fwd", "attn_fwd", "attn_merge"]
+        names = ["qk_norm_rope", "attn_fwd", "attn_fwd"] + ([] if args.fuse_merge else ["attn_merge"])
+
+        def attn(q_, k_, v_, out, lse, merge):
+            # The query prologue either ran in place on q (q_ = q) or runs in
+            # the attention's Q load (q_ = q0, --fuse-q).
+            if merge:
+                attn_fwd_ws_merge(q_, k_, v_, ws, out, lse, scale=scale)
+            elif args.fuse_q:
+                attn_fwd_ws_fused_q(q_, k_, v_, ws, w_q, cos_d, sin_d, cfg.eps, out=out, lse=lse, scale=scale)
+            else:
+                attn_fwd_ws(q_, k_, v_, ws, out=out, lse=lse, scale=scale)
 
         def step(ev):
-            q.copy_(q0)
             k.copy_(k0)
-            ev[0].record()
-            qk_norm_rope(q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
+            if args.fuse_q:
+                ev[0].record()
+                qk_norm_rope(None, k, None, w_k, cos_d, sin_d, cfg.eps)
+                q_ = q0
+            else:
+                q.copy_(q0)
+                ev[0].record()
+                qk_norm_rope(q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
+                q_ = q
             ev[1].record()
-            attn_fwd_ws(q, k[:, :, :c], v[:, :, :c], ws, out=out_a, lse=lse_a, scale=scale)
+            attn(q_, k[:, :, :c], v[:, :, :c], out_a, lse_a, False)
             ev[2].record()
-            attn_fwd_ws(q, k[:, :, c:], v[:, :, c:], ws, out=out_b, lse=lse_b, scale=scale)
-            ev[3].record()
-            attn_merge(out_a, lse_a, out_b, lse_b)
-            ev[4].record()
+            if args.fuse_merge:
+                attn(q_, k[:, :, c:], v[:, :, c:], out_a, lse_a, True)
+                ev[3].record()
+            else:
+                attn(q_, k[:, :, c:], v[:, :, c:], out_b, lse_b, False)
+                ev[3].record()
+                attn_merge(out_a, lse_a, out_b, lse_b)
+                ev[4].record()
 
         final_out, final_lse = out_a, lse_a
         merge_rows = B * H * Sq
         merge_bytes = merge_rows * (D * (4 + 4 + 4) + 12)
-        n_merge = 1
+        n_merge = 0 if args.fuse_merge else 1
     elif wl in ("qwen", "cosmos"):
         out = torch.empty((B, H, Sq, D), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
@@ -396,6 +399,9 @@ def main():
         attn_ms_total = sum(per_kernel["attn_fwd"]) / args.steps          # per step
         n_attn = launches["attn_fwd"]
         entry = "attn_fwd_ws (v_prep_kernel + attn_fwd_kernel per call)"
+        if wl == "wan" and args.fuse_merge:
+            entry = ("attn_fwd_ws + attn_fwd_ws_merge (v_prep_kernel + attn_fwd_kernel per call; the second "
+                     "merges into the first's output in its epilogue)")
     else:
         # Two streams: the interval spans both overlapped calls and the merge.
         attn_ms_total = sum(per_kernel["attn_fwd+attn_merge"]) / args.steps
@@ -431,7 +437,8 @@ def main():
         "wan": "Wan2.2-shaped attention step B1 H40 S75600 D128: QK RMSNorm+3D RoPE, ring-overlap "
                "attention (local 1/4 + remote 3/4 of the keys" + (", on two streams" if args.ring_streams == 2
                                                                   else "") + "), fp32 LSE merge"
-               + ("; query RMSNorm+RoPE fused into the attention's Q load" if args.fuse_q else ""),
+               + ("; query RMSNorm+RoPE fused into the attention's Q load" if args.fuse_q else "")
+               + ("; merge in the remote call's epilogue" if args.fuse_merge else ""),
         "qwen": "Qwen-Image joint attention B1 H24 S4312 D128: QK RMSNorm+RoPE, attention",
         "cosmos": "Cosmos-Predict video attention B2 H16 S12480 D128: QK RMSNorm+3D RoPE, attention",
         "sp": "Wan2.2 4-way SP share: Sq 18900 x Skv 75600 H40 D128 as 4 KV chunks + 3 fp32 merges",

@@ -8,6 +8,7 @@
  *   attn_fwd_varlen  the same over padded batches with per-batch lengths
  *   attn_fwd_ws_fused_q  attention with the query prologue fused into its Q load
  *   attn_fwd_ws_bsnd  attention storing its output into a head slice of a BSND tensor
+ *   attn_fwd_ws_merge  attention over one key chunk merged into a running (out, lse)
  *   attn_merge     fold of two partial attentions over disjoint key sets
  *   bsnd_to_bnsd, bnsd_to_bsnd  head-slice layout change of Ulysses sequence parallelism
  *
@@ -234,6 +235,28 @@ int attn_fwd_ws_bsnd(const void *q, const void *k, const void *v, int64_t kv_bh_
                      void *workspace, int64_t workspace_bytes, void *out, float *lse,
                      int B, int H, int Sq, int Skv, int D, float scale, int causal,
                      int out_dtype, int out_heads, int out_h0, hipStream_t stream);
+
+/*
+ * attn_fwd_ws over one key chunk, folded into a running partial result in
+ * the same call. [WAN] Ring Attention Overlap merges the attention of each
+ * key chunk into the running output through the LSEs; [PR274] item 2 does
+ * this with update_out_and_lse. Here the attention epilogue does the merge,
+ * so the chunk's output never goes to memory.
+ *
+ *   out_a  [B,H,Sq,D] of a_dtype (DIT_BF16 or DIT_FP32), read and written.
+ *          On entry it holds the attention of the same queries over other
+ *          keys (e.g. an attn_fwd_ws result).
+ *   lse_a  fp32 [B,H,Sq], read and written; required (NULL: DIT_ERR_NULL).
+ *
+ * The bits are those of attn_fwd_ws(q, k, v, ..., tmp, tmp_lse) with an fp32
+ * tmp, followed by attn_merge(out_a, lse_a, tmp, tmp_lse, ..., a_dtype,
+ * DIT_FP32). Other arguments and errors are as for attn_fwd_ws, with out_a
+ * in the place of out.
+ */
+int attn_fwd_ws_merge(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
+                      void *workspace, int64_t workspace_bytes, void *out_a, float *lse_a,
+                      int B, int H, int Sq, int Skv, int D, float scale, int causal,
+                      int a_dtype, hipStream_t stream);
 
 /*
  * Merge of two partial attentions over disjoint key sets, in place into

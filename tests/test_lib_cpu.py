@@ -48,6 +48,7 @@ def lib():
     lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
                                         i32, p]
     lib.attn_fwd_ws_bsnd.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, p]
+    lib.attn_fwd_ws_merge.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
     lib.attn_fwd_varlen.argtypes = [p, p, p, p, i64, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
@@ -60,7 +61,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
-                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd",
+                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd",
                           "bnsd_to_bsnd", "dit_attn_status_string",
                           "dit_attn_version"}, names
     for name in names:
@@ -204,6 +205,22 @@ def test_attn_fwd_ws_bsnd_rejections(lib):
     assert call(lse=O + out_bytes - 1024) == ALIAS       # lse inside the BSND extent
     assert call(ws=O + out_bytes - need + 16) == ALIAS   # workspace runs into out
     assert call(dt=FP32, ws=O + out_bytes) == ALIAS      # fp32 out is twice as long
+
+
+def test_attn_fwd_ws_merge_rejections(lib):
+    f = lib.attn_fwd_ws_merge
+    need = 2 * 4 * 64 * 64 * 2
+
+    def call(ws=WS, o=O, lse=L, dt=FP32, nbytes=need):
+        return f(Q, K, V, 256 * 64, ws, nbytes, o, lse, 1, 2, 256, 256, 64, 0.125, 0, dt, None)
+
+    assert call(ws=None) == NULL
+    assert call(lse=None) == NULL                        # the running LSE is required
+    assert call(o=None) == NULL
+    assert call(dt=7) == UNSUP
+    assert call(nbytes=need - 1) == SHAPE
+    assert call(lse=O + 1024) == ALIAS                   # lse inside out_a
+    assert call(ws=L) == ALIAS
 
 
 def test_qk_norm_rope_rejections(lib):
