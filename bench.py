@@ -26,7 +26,8 @@ fp64 oracle on a bounded sample of query rows on the host cores.
 
 Other workloads (--workload) are per-config measurements:
   qwen / cosmos: restore, prologue, attn_fwd_ws over all keys;
-  sp: 4 x attn_fwd_ws over KV chunks of 18900 keys + 3 fp32 merges (Sq 18900).
+  sp: attn_fwd_ws + 3 x attn_fwd_ws_merge over KV chunks of 18900 keys (Sq 18900);
+      --separate-merge: 4 x attn_fwd_ws + 3 fp32 attn_merge.
 """
 from __future__ import annotations
 
@@ -345,25 +346,29 @@ def main():
         cs = Skv // n
         outs = [torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev) for _ in range(n)]
         lses = [torch.empty((B, H, Sq), dtype=torch.float32, device=dev) for _ in range(n)]
-        names = ["attn_fwd"] * n + ["attn_merge"] * (n - 1)
+        names = ["attn_fwd"] * n + ([] if args.fuse_merge else ["attn_merge"] * (n - 1))
 
         def step(ev):
             i_ev = 0
             ev[i_ev].record()
             for i in range(n):
-                attn_fwd_ws(q0, k0[:, :, i * cs:(i + 1) * cs], v[:, :, i * cs:(i + 1) * cs], ws, out=outs[i],
-                            lse=lses[i], scale=scale)
+                kc, vc = k0[:, :, i * cs:(i + 1) * cs], v[:, :, i * cs:(i + 1) * cs]
+                if args.fuse_merge and i > 0:
+                    attn_fwd_ws_merge(q0, kc, vc, ws, outs[0], lses[0], scale=scale)
+                else:
+                    attn_fwd_ws(q0, kc, vc, ws, out=outs[i], lse=lses[i], scale=scale)
                 i_ev += 1
                 ev[i_ev].record()
-            for i in range(1, n):
-                attn_merge(outs[0], lses[0], outs[i], lses[i])
-                i_ev += 1
-                ev[i_ev].record()
+            if not args.fuse_merge:
+                for i in range(1, n):
+                    attn_merge(outs[0], lses[0], outs[i], lses[i])
+                    i_ev += 1
+                    ev[i_ev].record()
 
         final_out, final_lse = outs[0], lses[0]
         merge_rows = B * H * Sq
         merge_bytes = merge_rows * (D * (4 + 4 + 4) + 12)
-        n_merge = n - 1
+        n_merge = 0 if args.fuse_merge else n - 1
 
     n_ev = len(names) + 1
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]  # noqa: E731
@@ -399,7 +404,7 @@ def main():
         attn_ms_total = sum(per_kernel["attn_fwd"]) / args.steps          # per step
         n_attn = launches["attn_fwd"]
         entry = "attn_fwd_ws (v_prep_kernel + attn_fwd_kernel per call)"
-        if wl == "wan" and args.fuse_merge:
+        if wl in ("wan", "sp") and args.fuse_merge:
             entry = ("attn_fwd_ws + attn_fwd_ws_merge (v_prep_kernel + attn_fwd_kernel per call; the second "
                      "merges into the first's output in its epilogue)")
     else:
@@ -441,7 +446,8 @@ def main():
                + ("; merge in the remote call's epilogue" if args.fuse_merge else ""),
         "qwen": "Qwen-Image joint attention B1 H24 S4312 D128: QK RMSNorm+RoPE, attention",
         "cosmos": "Cosmos-Predict video attention B2 H16 S12480 D128: QK RMSNorm+3D RoPE, attention",
-        "sp": "Wan2.2 4-way SP share: Sq 18900 x Skv 75600 H40 D128 as 4 KV chunks + 3 fp32 merges",
+        "sp": "Wan2.2 4-way SP share: Sq 18900 x Skv 75600 H40 D128 as 4 KV chunks"
+              + (" merged in the attention epilogue" if args.fuse_merge else " + 3 fp32 merges"),
     }[wl]
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
