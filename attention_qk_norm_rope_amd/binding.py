@@ -43,6 +43,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     p, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.qk_norm_rope.argtypes = [p, p, p, p, p, p, f32, i32, i32, i32, i32, p]
+    lib.qk_norm_rope_out.argtypes = [p, p, p, p, p, p, p, p, f32, i32, i32, i32, i32, p]
     lib.attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_kv_strided.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_ws.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
@@ -57,7 +58,7 @@ def _load():
     lib.attn_fwd_varlen.argtypes = [p, p, p, p, i64, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
-    for name in ("qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_fwd_ws_fused_q",
+    for name in ("qk_norm_rope", "qk_norm_rope_out", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_fwd_ws_fused_q",
                  "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
@@ -140,6 +141,39 @@ def qk_norm_rope(q, k, w_q, w_k, cos, sin, eps: float):
                               float(eps), B, H, S, D, _stream())
     _check("qk_norm_rope", st)
     return q, k
+
+
+def qk_norm_rope_out(q, k, q_out, k_out, w_q, w_k, cos, sin, eps: float):
+    """qk_norm_rope into separate outputs: q_out <- prologue(q), k_out <-
+    prologue(k), inputs left intact (an output may also be its own input).
+    Either pair may be None.  Same bits as the in-place form.  Returns
+    (q_out, k_out)."""
+    ref = q if q is not None else k
+    if ref is None:
+        raise ValueError("q and k are both None")
+    if (q is None) != (q_out is None) or (k is None) != (k_out is None):
+        raise ValueError("an input and its output must both be given or both be None")
+    dev = ref.device
+    B, H, S, D = ref.shape
+    for t, name in ((q, "q"), (k, "k"), (q_out, "q_out"), (k_out, "k_out")):
+        if t is not None:
+            _need(t, name, torch.bfloat16, dev)
+            if tuple(t.shape) != (B, H, S, D) or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous [{B},{H},{S},{D}]")
+    for t, name, use in ((w_q, "w_q", q is not None), (w_k, "w_k", k is not None)):
+        if use:
+            _need(t, name, torch.float32, dev)
+            if tuple(t.shape) != (D,) or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous [{D}]")
+    for t, name in ((cos, "cos"), (sin, "sin")):
+        _need(t, name, torch.float32, dev)
+        if tuple(t.shape) != (S, D) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [{S},{D}]")
+    st = _load().qk_norm_rope_out(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out),
+                                  _ptr(w_q if q is not None else None), _ptr(w_k if k is not None else None),
+                                  _ptr(cos), _ptr(sin), float(eps), B, H, S, D, _stream())
+    _check("qk_norm_rope_out", st)
+    return q_out, k_out
 
 
 def _kv_bh_stride(t, B, H, S, D) -> int | None:

@@ -27,12 +27,12 @@ constexpr int64_t kMaxElems = (int64_t)1 << 46;  // keeps every byte count far f
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-int qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k, const float* cos_t,
-                 const float* sin_t, float eps, int B, int H, int S, int D, hipStream_t stream) {
+// Checks of qk_norm_rope / qk_norm_rope_out; q_in == q (k_in == k) is the
+// in-place form.  A destination may coincide exactly with its own source but
+// must not overlap anything else it does not own.
+int prologue_common(const void* q_in, const void* k_in, void* q, void* k, const float* w_q, const float* w_k,
+                    const float* cos_t, const float* sin_t, float eps, int B, int H, int S, int D,
+                    hipStream_t stream) {
     if ((!q && !k) || !cos_t || !sin_t) return DIT_ERR_NULL;
     if ((q && !w_q) || (k && !w_k)) return DIT_ERR_NULL;
     if (B < 1 || H < 1 || S < 1 || D < 1) return DIT_ERR_SHAPE;
@@ -41,21 +41,43 @@ int qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k, const flo
     const int64_t BH = (int64_t)B * H;
     const int64_t elems = BH * S * D;
     if (BH > 0x7FFFFFFF || elems > kMaxElems) return DIT_ERR_SHAPE;
-    if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)) || !aligned(cos_t, 16) || !aligned(sin_t, 16) ||
-        (w_q && q && !aligned(w_q, 16)) || (w_k && k && !aligned(w_k, 16)))
+    if ((q && (!aligned(q, 16) || !aligned(q_in, 16))) || (k && (!aligned(k, 16) || !aligned(k_in, 16))) ||
+        !aligned(cos_t, 16) || !aligned(sin_t, 16) || (q && !aligned(w_q, 16)) || (k && !aligned(w_k, 16)))
         return DIT_ERR_ALIGN;
     const Range rq = range_of(q, q ? elems * 2 : 0), rk = range_of(k, k ? elems * 2 : 0);
+    const Range rqi = range_of(q_in, q ? elems * 2 : 0), rki = range_of(k_in, k ? elems * 2 : 0);
     const Range rc = range_of(cos_t, (int64_t)S * D * 4), rs = range_of(sin_t, (int64_t)S * D * 4);
     const Range rwq = range_of(w_q, q ? (int64_t)D * 4 : 0), rwk = range_of(w_k, k ? (int64_t)D * 4 : 0);
+    auto same = [](Range a, Range b) { return a.lo == b.lo && a.hi == b.hi; };
     if (q && k && overlap(rq, rk)) return DIT_ERR_ALIAS;
-    for (Range out : {rq, rk}) {
+    const Range outs[2] = {rq, rk}, own[2] = {rqi, rki}, other[2] = {rki, rqi};
+    for (int i = 0; i < 2; ++i) {
+        const Range out = outs[i];
         if (out.lo == out.hi) continue;
         for (Range in : {rc, rs, rwq, rwk})
             if (in.lo != in.hi && overlap(out, in)) return DIT_ERR_ALIAS;
+        if (overlap(out, own[i]) && !same(out, own[i])) return DIT_ERR_ALIAS;
+        if (other[i].lo != other[i].hi && overlap(out, other[i])) return DIT_ERR_ALIAS;
     }
     (void)hipGetLastError();  // report only this launch's error
-    return hip_status(dit::launch_qk_norm_rope(q, k, q ? w_q : nullptr, k ? w_k : nullptr, cos_t, sin_t,
-                                               eps, (int)BH, S, D, stream));
+    return hip_status(dit::launch_qk_norm_rope(q ? q_in : nullptr, k ? k_in : nullptr, q, k, q ? w_q : nullptr,
+                                               k ? w_k : nullptr, cos_t, sin_t, eps, (int)BH, S, D, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k, const float* cos_t,
+                 const float* sin_t, float eps, int B, int H, int S, int D, hipStream_t stream) {
+    return prologue_common(q, k, q, k, w_q, w_k, cos_t, sin_t, eps, B, H, S, D, stream);
+}
+
+int qk_norm_rope_out(const void* q_in, const void* k_in, void* q_out, void* k_out, const float* w_q,
+                     const float* w_k, const float* cos_t, const float* sin_t, float eps, int B, int H, int S,
+                     int D, hipStream_t stream) {
+    if ((q_in == nullptr) != (q_out == nullptr) || (k_in == nullptr) != (k_out == nullptr)) return DIT_ERR_NULL;
+    return prologue_common(q_in, k_in, q_out, k_out, w_q, w_k, cos_t, sin_t, eps, B, H, S, D, stream);
 }
 
 }  // extern "C"

@@ -38,9 +38,10 @@ int64_t v_prep_bytes(int64_t BH, int Skv, int D);
 hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D, const int* lkv,
                          int Hkv, hipStream_t stream);
 
-// RMSNorm + interleaved rotary, in place; q or k may be null.
-hipError_t launch_qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k,
-                               const float* cos_t, const float* sin_t, float eps, int BH, int S,
+// RMSNorm + interleaved rotary of q_src/k_src into q/k (equal pointers: in
+// place); a tensor whose source is null is skipped.
+hipError_t launch_qk_norm_rope(const void* q_src, const void* k_src, void* q, void* k, const float* w_q,
+                               const float* w_k, const float* cos_t, const float* sin_t, float eps, int BH, int S,
                                int D, hipStream_t stream);
 
 // BSND [B,S,H,D] head slice [h0, h0+Hs) <-> BNSD [B,Hs,S,D] (2-byte elements).

@@ -1,5 +1,5 @@
-// Per-head RMSNorm + interleaved rotary embedding of q and k, in place, for
-// gfx950.  HBM-bound: one 16-byte read and one 16-byte write per 8 elements.
+// Per-head RMSNorm + interleaved rotary embedding of q and k, in place or
+// into separate outputs, for gfx950.  HBM-bound: one 16-byte read and one 16-byte write per 8 elements.
 //
 // Operation: RMSNorm of "Cosmos 昇腾 NPU 多卡并行优化说明" §3.2 and the rms_norm
 // section of "NPU Wan2.2-I2V模型推理优化实践" (mean of squares over the head
@@ -33,12 +33,14 @@ constexpr int UNR = 8;       // rows in flight per thread
 
 template <int D>
 __global__ void __launch_bounds__(256)
-qk_norm_rope_kernel(uint16_t* __restrict__ q, uint16_t* __restrict__ k, const float* __restrict__ w_q,
-                    const float* __restrict__ w_k, const float* __restrict__ cos_t,
+qk_norm_rope_kernel(const uint16_t* q_src, const uint16_t* k_src, uint16_t* q_dst, uint16_t* k_dst,
+                    const float* __restrict__ w_q, const float* __restrict__ w_k, const float* __restrict__ cos_t,
                     const float* __restrict__ sin_t, float eps, int BH, int S) {
     constexpr int L = D / 8;               // lanes per row
     constexpr int RPB = 256 / L;           // sequence positions per block
-    uint16_t* x = blockIdx.y == 0 ? q : k;
+    // Source and destination are equal for the in-place form (no restrict).
+    const uint16_t* x = blockIdx.y == 0 ? q_src : k_src;
+    uint16_t* y = blockIdx.y == 0 ? q_dst : k_dst;
     const float* w = blockIdx.y == 0 ? w_q : w_k;
     if (x == nullptr) return;
     // All L lanes of a row share s, so a row group leaves (or stays) as a
@@ -88,31 +90,32 @@ qk_norm_rope_kernel(uint16_t* __restrict__ q, uint16_t* __restrict__ k, const fl
             for (int i = 0; i < 4; ++i)
                 res[i] = nr::pair(xv[2 * i], xv[2 * i + 1], inv_r, wv[2 * i], wv[2 * i + 1], cv[2 * i],
                                   cv[2 * i + 1], sv[2 * i], sv[2 * i + 1]);
-            *(u32x4*)(x + ((int64_t)(bh + u) * S + s) * D + d0) = res;
+            *(u32x4*)(y + ((int64_t)(bh + u) * S + s) * D + d0) = res;
         }
     }
     }
 }
 
 template <int D>
-hipError_t launch(void* q, void* k, const float* w_q, const float* w_k, const float* cos_t,
-                  const float* sin_t, float eps, int BH, int S, hipStream_t stream) {
+hipError_t launch(const void* q_src, const void* k_src, void* q, void* k, const float* w_q, const float* w_k,
+                  const float* cos_t, const float* sin_t, float eps, int BH, int S, hipStream_t stream) {
     constexpr int RPB = 256 / (D / 8);
     const unsigned gx = (unsigned)((S + RPB - 1) / RPB);
     int64_t gz = ((int64_t)BH + HB - 1) / HB;
     if (gz > 65535) gz = 65535;
     hipLaunchKernelGGL((qk_norm_rope_kernel<D>), dim3(gx, 2, (unsigned)gz), dim3(256), 0, stream,
-                       (uint16_t*)q, (uint16_t*)k, w_q, w_k, cos_t, sin_t, eps, BH, S);
+                       (const uint16_t*)q_src, (const uint16_t*)k_src, (uint16_t*)q, (uint16_t*)k, w_q, w_k, cos_t,
+                       sin_t, eps, BH, S);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_qk_norm_rope(void* q, void* k, const float* w_q, const float* w_k,
-                               const float* cos_t, const float* sin_t, float eps, int BH, int S,
+hipError_t launch_qk_norm_rope(const void* q_src, const void* k_src, void* q, void* k, const float* w_q,
+                               const float* w_k, const float* cos_t, const float* sin_t, float eps, int BH, int S,
                                int D, hipStream_t stream) {
-    if (D == 128) return launch<128>(q, k, w_q, w_k, cos_t, sin_t, eps, BH, S, stream);
-    return launch<64>(q, k, w_q, w_k, cos_t, sin_t, eps, BH, S, stream);
+    if (D == 128) return launch<128>(q_src, k_src, q, k, w_q, w_k, cos_t, sin_t, eps, BH, S, stream);
+    return launch<64>(q_src, k_src, q, k, w_q, w_k, cos_t, sin_t, eps, BH, S, stream);
 }
 
 }  // namespace dit

@@ -7,8 +7,9 @@
 One step is one pass of the whole path over one batch of synthetic input.
 Default workload (Wan2.2 shape, B1 H40 S75600 D128, bf16 ~ N(0,1)), laid out
 as the Ring Attention Overlap of the Wan2.2 NPU page on one GPU:
-  1. restore q, k from pristine device copies (the prologue works in place),
-  2. qk_norm_rope(q, k): per-head RMSNorm (eps 1e-5) + 3D interleaved RoPE,
+  1. (nothing to restore: the prologue reads the pristine q0, k0)
+  2. qk_norm_rope_out(q0, k0 -> q, k): per-head RMSNorm (eps 1e-5) + 3D
+     interleaved RoPE into the tensors the attention reads,
   3. attn_fwd_ws over the local quarter of the keys   -> fp32 out_a, lse_a,
   4. attn_fwd_ws_merge over the remaining three quarters (a window of the
      same K/V), whose epilogue merges each row into (out_a, lse_a) with the
@@ -25,7 +26,7 @@ kernels are launched on (torch's current stream).  The CPU baseline times the
 fp64 oracle on a bounded sample of query rows on the host cores.
 
 Other workloads (--workload) are per-config measurements:
-  qwen / cosmos: restore, prologue, attn_fwd_ws over all keys;
+  qwen / cosmos: prologue (out of place), attn_fwd_ws over all keys;
   sp: attn_fwd_ws + 3 x attn_fwd_ws_merge over KV chunks of 18900 keys (Sq 18900);
       --separate-merge: 4 x attn_fwd_ws + 3 fp32 attn_merge.
 """
@@ -215,7 +216,7 @@ def main():
 
     from attention_qk_norm_rope_amd import (attn_fwd_ring_overlap, attn_fwd_workspace_bytes, attn_fwd_ws,
                                             attn_fwd_ws_fused_q, attn_fwd_ws_merge, attn_merge, inputs,
-                                            qk_norm_rope)
+                                            qk_norm_rope, qk_norm_rope_out)
     from attention_qk_norm_rope_amd import binding
 
     if not torch.cuda.is_available():
@@ -269,10 +270,8 @@ def main():
         names = ["qk_norm_rope", "attn_fwd+attn_merge"]
 
         def step(ev):
-            q.copy_(q0)
-            k.copy_(k0)
             ev[0].record()
-            qk_norm_rope(q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
+            qk_norm_rope_out(q0, k0, q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
             ev[1].record()
             attn_fwd_ring_overlap(q, k, v, c, ws_local, ws, out_local=out_a, lse_local=lse_a, out_remote=out_b,
                                   lse_remote=lse_b, scale=scale, side_stream=side)
@@ -299,15 +298,12 @@ def main():
                 attn_fwd_ws(q_, k_, v_, ws, out=out, lse=lse, scale=scale)
 
         def step(ev):
-            k.copy_(k0)
+            ev[0].record()
             if args.fuse_q:
-                ev[0].record()
-                qk_norm_rope(None, k, None, w_k, cos_d, sin_d, cfg.eps)
+                qk_norm_rope_out(None, k0, None, k, None, w_k, cos_d, sin_d, cfg.eps)
                 q_ = q0
             else:
-                q.copy_(q0)
-                ev[0].record()
-                qk_norm_rope(q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
+                qk_norm_rope_out(q0, k0, q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
                 q_ = q
             ev[1].record()
             attn(q_, k[:, :, :c], v[:, :, :c], out_a, lse_a, False)
@@ -331,10 +327,8 @@ def main():
         names = ["qk_norm_rope", "attn_fwd"]
 
         def step(ev):
-            q.copy_(q0)
-            k.copy_(k0)
             ev[0].record()
-            qk_norm_rope(q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
+            qk_norm_rope_out(q0, k0, q, k, w_q, w_k, cos_d, sin_d, cfg.eps)
             ev[1].record()
             attn_fwd_ws(q, k, v, ws, out=out, lse=lse, scale=scale)
             ev[2].record()

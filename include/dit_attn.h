@@ -3,6 +3,7 @@
  * path of video and image diffusion transformers:
  *
  *   qk_norm_rope   per-head RMSNorm of q and k, then interleaved rotary, in place
+ *   qk_norm_rope_out  the same into separate outputs
  *   attn_fwd       softmax(scale * Q K^T) V with a per-row log-sum-exp (BNSD)
  *   attn_fwd_gqa   the same with Hkv K/V heads shared by H query heads
  *   attn_fwd_varlen  the same over padded batches with per-batch lengths
@@ -86,6 +87,25 @@ enum dit_attn_dtype {
 int qk_norm_rope(void *q, void *k, const float *w_q, const float *w_k,
                  const float *cos, const float *sin, float eps,
                  int B, int H, int S, int D, hipStream_t stream);
+
+/*
+ * qk_norm_rope writing its results to separate outputs: q_out <- the
+ * normalised, rotated q_in, and k_out <- that of k_in, with the same
+ * arithmetic and bits as the in-place form. A model's projections produce
+ * fresh q and k every layer, so the in-place form suits them. This form
+ * keeps the inputs intact.
+ *
+ *   q_in, k_in    bf16 [B,H,S,D], read only. q_in and q_out are both NULL
+ *                 or both given (same for k); not all four NULL.
+ *   q_out, k_out  bf16 [B,H,S,D], written. An output may be exactly its own
+ *                 input (the in-place form); otherwise it must not overlap
+ *                 either input, the other output, the tables or the weights.
+ * Other arguments and errors are as for qk_norm_rope. DIT_ERR_NULL when an
+ * input and its output are not both given.
+ */
+int qk_norm_rope_out(const void *q_in, const void *k_in, void *q_out, void *k_out,
+                     const float *w_q, const float *w_k, const float *cos, const float *sin,
+                     float eps, int B, int H, int S, int D, hipStream_t stream);
 
 /*
  * Flash attention forward with per-row LSE.  [COSMOS] §3.1 and [WAN]

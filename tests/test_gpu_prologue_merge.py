@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from oracle import compare
-from attention_qk_norm_rope_amd import attn_merge, inputs, qk_norm_rope
+from attention_qk_norm_rope_amd import attn_merge, inputs, qk_norm_rope, qk_norm_rope_out
 from gpu_common import dev_bits, dev_f32, host_bits, host_f64, say
 
 pytestmark = pytest.mark.gpu
@@ -52,6 +52,34 @@ def test_prologue_single_tensor_and_table_slice():
     qk_norm_rope(dq, None, dev_f32(w), None, c[:S], s[:S], 1e-5)
     ref = oracle.qk_norm_rope(q, w, full_cos[:S], full_sin[:S], 1e-5)
     compare.assert_ok(compare.prologue_report(host_f64(dq), ref), "q-only prologue")
+
+
+@pytest.mark.parametrize("B,H,S,D", [(1, 3, 300, 128), (2, 41, 19, 64)])
+def test_prologue_out_of_place(B, H, S, D):
+    """qk_norm_rope_out gives the bits of the in-place form, leaves its inputs
+    untouched, and also accepts an output that is its own input."""
+    q = inputs.random_bits(S + 11, (B, H, S, D), std=1.5)
+    k = inputs.random_bits(S + 12, (B, H, S, D))
+    rng = np.random.default_rng(S + 13)
+    w_q = dev_f32(rng.uniform(0.5, 1.5, D).astype(np.float32))
+    w_k = dev_f32(rng.uniform(0.5, 1.5, D).astype(np.float32))
+    cos, sin = inputs.rope_tables(inputs.rope_positions(("line", S)), D)
+    c, s_ = dev_f32(cos), dev_f32(sin)
+    say(f"[prologue] out of place B{B} H{H} S{S} D{D}")
+    dq, dk = dev_bits(q), dev_bits(k)
+    qo, ko = torch.empty_like(dq), torch.empty_like(dk)
+    qk_norm_rope_out(dq, dk, qo, ko, w_q, w_k, c, s_, 1e-6)
+    qi, ki = dq.clone(), dk.clone()
+    qk_norm_rope(qi, ki, w_q, w_k, c, s_, 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(dq), q) and np.array_equal(host_bits(dk), k), "an input was modified"
+    assert torch.equal(qo, qi) and torch.equal(ko, ki), "out-of-place bits differ from in-place"
+    # q in place through the out-of-place entry, k alone skipped
+    qk_norm_rope_out(dq, None, dq, None, w_q, None, c, s_, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, qi)
+    ref = oracle.qk_norm_rope(k, host_f64(w_k).astype(np.float32), cos, sin, 1e-6)
+    compare.assert_ok(compare.prologue_report(host_f64(ko), ref), "out-of-place prologue")
 
 
 def test_prologue_identity_table_is_rmsnorm_bits():

@@ -39,6 +39,7 @@ def lib():
     lib = ctypes.CDLL(LIB)
     p, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.qk_norm_rope.argtypes = [p, p, p, p, p, p, f32, i32, i32, i32, i32, p]
+    lib.qk_norm_rope_out.argtypes = [p, p, p, p, p, p, p, p, f32, i32, i32, i32, i32, p]
     lib.attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_kv_strided.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_ws.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
@@ -60,7 +61,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert set(names) == {"qk_norm_rope", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
+    assert set(names) == {"qk_norm_rope", "qk_norm_rope_out", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
                           "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd",
                           "bnsd_to_bsnd", "dit_attn_status_string",
                           "dit_attn_version"}, names
@@ -221,6 +222,26 @@ def test_attn_fwd_ws_merge_rejections(lib):
     assert call(nbytes=need - 1) == SHAPE
     assert call(lse=O + 1024) == ALIAS                   # lse inside out_a
     assert call(ws=L) == ALIAS
+
+
+def test_qk_norm_rope_out_rejections(lib):
+    f = lib.qk_norm_rope_out
+    n = 2 * 256 * 64 * 2                                 # bytes of one [1,2,256,64] bf16 tensor
+    QO, KO = 0x30_0000_0000, 0x31_0000_0000
+
+    def call(qi=Q, ki=K, qo=QO, ko=KO, wq=W1, wk=W2, c=C, s=S_):
+        return f(qi, ki, qo, ko, wq, wk, c, s, 1e-6, 1, 2, 256, 64, None)
+
+    assert call(qo=None) == NULL                         # an input without its output
+    assert call(ki=None) == NULL                         # an output without its input
+    assert call(qi=None, ki=None, qo=None, ko=None) == NULL
+    assert call(qo=QO + 8) == ALIGN
+    assert call(ki=K + 8) == ALIGN                       # inputs are checked too
+    assert call(qo=Q + 1024) == ALIAS                    # partial overlap with its own input
+    assert call(qo=K) == ALIAS                           # onto the other input
+    assert call(ko=QO + n - 16) == ALIAS                 # the two outputs overlap
+    assert call(qo=C) == ALIAS                           # onto a table
+    assert call(ko=W1) == ALIAS                          # onto a weight
 
 
 def test_qk_norm_rope_rejections(lib):
