@@ -15,8 +15,8 @@ gives one PCG64 stream per [S, D] slab -- stream t*B*H + b*H + h fills slab
 in C order -- and the last stream draws w_q then w_k ~ U(0.5, 1.5) as float32
 [D].  q, k, v are rounded to bf16 (round to nearest even) once.  Independent
 streams let the slabs be filled in parallel with a result that does not
-depend on the thread count.  The seed is the config number; config 5 reuses
-config 4's tensors.
+depend on the thread count.  The seed is the workload number; the Wan2.2 SP share (5) reuses
+the Wan2.2 workload's (4) tensors.
 """
 from __future__ import annotations
 
@@ -66,7 +66,7 @@ def times_four_bits(bits) -> np.ndarray:
 
 @dataclasses.dataclass(frozen=True)
 class Config:
-    index: int
+    index: int                 # workload number: seeds the inputs and the sampled rows
     name: str
     B: int
     H: int
@@ -75,7 +75,7 @@ class Config:
     seed: int
     eps: float | None          # prologue epsilon (None: no prologue in this config)
     grid: tuple | None         # rotary position grid, see rope_positions()
-    sq: int | None = None      # query rows when different from S (config 5)
+    sq: int | None = None      # query rows when different from S (the SP share)
     chunks: int = 1            # KV chunks merged with attn_merge
 
     @property
@@ -95,12 +95,12 @@ class Config:
         return f / 2 if causal else f
 
 
-CONFIGS = {
-    1: Config(1, "tiny B1 H2 S256 D64", 1, 2, 256, 64, 1, 1e-6, ("line", 256), chunks=2),
-    2: Config(2, "Qwen-Image joint B1 H24 S4312 D128", 1, 24, 4312, 128, 2, 1e-6, ("qwen", 78, 52, 256)),
-    3: Config(3, "Cosmos-Predict video B2 H16 S12480 D128", 2, 16, 12480, 128, 3, 1e-6, ("video", 8, 30, 52)),
-    4: Config(4, "Wan2.2 long video B1 H40 S75600 D128", 1, 40, 75600, 128, 4, 1e-5, ("video", 21, 45, 80)),
-    5: Config(5, "Wan2.2 4-way SP share Sq18900 Skv75600 H40 D128", 1, 40, 75600, 128, 4, None, None,
+WORKLOADS = {
+    "tiny": Config(1, "tiny B1 H2 S256 D64", 1, 2, 256, 64, 1, 1e-6, ("line", 256), chunks=2),
+    "qwen": Config(2, "Qwen-Image joint B1 H24 S4312 D128", 1, 24, 4312, 128, 2, 1e-6, ("qwen", 78, 52, 256)),
+    "cosmos": Config(3, "Cosmos-Predict video B2 H16 S12480 D128", 2, 16, 12480, 128, 3, 1e-6, ("video", 8, 30, 52)),
+    "wan": Config(4, "Wan2.2 long video B1 H40 S75600 D128", 1, 40, 75600, 128, 4, 1e-5, ("video", 21, 45, 80)),
+    "wan_sp": Config(5, "Wan2.2 4-way SP share Sq18900 Skv75600 H40 D128", 1, 40, 75600, 128, 4, None, None,
               sq=18900, chunks=4),
 }
 
@@ -119,7 +119,7 @@ def _workers() -> int:
 def make_inputs(cfg: Config) -> dict:
     """q, k, v (bf16 bits, [B,H,S,D]) and w_q, w_k (fp32 [D]) for a config.
 
-    For config 5 the returned q is config 4's q restricted to rows [0, Sq).
+    For the SP share (5) the returned q is the Wan2.2 workload's q restricted to rows [0, Sq).
     """
     B, H, S, D = cfg.B, cfg.H, cfg.S, cfg.D
     streams = np.random.SeedSequence(cfg.seed).spawn(3 * B * H + 1)
@@ -212,7 +212,7 @@ def rope_tables(positions: np.ndarray, D: int, theta: float = 10000.0):
 
 def config_rope_tables(cfg: Config):
     if cfg.grid is None:
-        raise ValueError(f"config {cfg.index} has no prologue")
+        raise ValueError(f"workload {cfg.name} has no prologue")
     pos = rope_positions(cfg.grid)
     if pos.shape[0] != cfg.S:
         raise ValueError("grid size does not match S")

@@ -207,8 +207,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the path would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the design notes "
+              "describe how the path would shard). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -230,8 +230,8 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     wl = args.workload
-    cfg = {"wan": inputs.CONFIGS[4], "qwen": inputs.CONFIGS[2], "cosmos": inputs.CONFIGS[3],
-           "sp": inputs.CONFIGS[5]}[wl]
+    cfg = {"wan": inputs.WORKLOADS["wan"], "qwen": inputs.WORKLOADS["qwen"], "cosmos": inputs.WORKLOADS["cosmos"],
+           "sp": inputs.WORKLOADS["wan_sp"]}[wl]
     log(f"[bench] generating inputs for {cfg.name}")
     t0 = time.time()
     x = inputs.make_inputs(cfg)

@@ -46,7 +46,7 @@ def rows_of(t: torch.Tensor, rows: np.ndarray) -> np.ndarray:
 
 
 @functools.lru_cache(maxsize=2)
-def workload(index: int) -> dict:
+def workload(name: str) -> dict:
     """Host inputs of a config (cached for the session)."""
-    say(f"[inputs] generating config {index}")
-    return inputs.make_inputs(inputs.CONFIGS[index])
+    say(f"[inputs] generating workload {name}")
+    return inputs.make_inputs(inputs.WORKLOADS[name])

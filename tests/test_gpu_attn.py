@@ -135,7 +135,7 @@ def test_kv_window_equals_contiguous_chunk():
 def test_split_merge_equals_full_and_differs_from_local_only():
     """The ring bug on the pages returned the local chunk's result unchanged;
     a 2-chunk attn_fwd + attn_merge must instead equal full attention."""
-    cfg = inputs.CONFIGS[1]
+    cfg = inputs.WORKLOADS["tiny"]
     x = inputs.make_inputs(cfg)
     q, k, v = x["q"], x["k"], x["v"]
     kc, vc = inputs.split_kv(k, 2), inputs.split_kv(v, 2)

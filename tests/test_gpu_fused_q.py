@@ -65,14 +65,14 @@ def test_fused_q_small(case):
 def test_fused_q_qwen_workload():
     """The Qwen-Image-shaped workload (B1 H24 S4312 D128, its RoPE grid and
     weights): fused equals unfused, and the oracle agrees on sampled rows."""
-    cfg = inputs.CONFIGS[2]
-    x = workload(2)
+    cfg = inputs.WORKLOADS["qwen"]
+    x = workload("qwen")
     cos, sin = inputs.config_rope_tables(cfg)
-    say("[fused_q] config 2")
+    say("[fused_q] qwen workload")
     dq2, dk, o, l = _run(x["q"], x["k"], x["v"], x["w_q"], x["w_k"], cos, sin, cfg.eps, cfg.scale, False,
                          torch.bfloat16)
     rows = inputs.sample_rows(cfg.index, cfg.B, cfg.H, cfg.Sq)
     ref_o, ref_l = oracle.attn(host_bits(dq2), host_bits(dk), x["v"], cfg.scale, False, rows=rows)
     rep = compare.attn_report(rows_of(o, rows), ref_o, rows_of(l, rows), ref_l)
-    say(f"[fused_q] config 2: {rep}")
-    compare.assert_ok(rep, "fused q config 2")
+    say(f"[fused_q] qwen workload: {rep}")
+    compare.assert_ok(rep, "fused q qwen workload")

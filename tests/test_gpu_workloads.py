@@ -3,7 +3,7 @@
 The prologue is compared on every element.  Attention is compared on a
 seeded sample of query rows per (b,h) (rows 0, 127, 128, the ragged tail,
 the last row and uniform draws), with the oracle consuming the GPU
-prologue's bf16 output, so stage errors do not compound.  Config 5 checks
+prologue's bf16 output, so stage errors do not compound.  The Wan2.2 SP-share workload checks
 the 4-chunk ring chain with an fp32 accumulator and with bf16 chunk outputs
 and accumulator, and the all-gather path (Skv = 75600 in one call).
 """
@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 def _prologue(cfg, x):
     cos, sin = inputs.config_rope_tables(cfg)
     dq, dk = dev_bits(x["q"]), dev_bits(x["k"])
-    say(f"[config {cfg.index}] prologue")
+    say(f"[{cfg.name}] prologue")
     qk_norm_rope(dq, dk, dev_f32(x["w_q"]), dev_f32(x["w_k"]), dev_f32(cos), dev_f32(sin), cfg.eps)
     torch.cuda.synchronize()
     return dq, dk, cos, sin
@@ -38,28 +38,28 @@ def _check_prologue_heads(cfg, x, dq, dk, cos, sin, heads=None):
             ref = oracle.qk_norm_rope(np.ascontiguousarray(src[:, heads]), w, cos, sin, cfg.eps)
             out = host_f64(got[:, heads])
         rep = compare.prologue_report(out, ref)
-        say(f"[config {cfg.index}] prologue {name}: {rep}")
-        compare.assert_ok(rep, f"config {cfg.index} prologue {name}")
+        say(f"[{cfg.name}] prologue {name}: {rep}")
+        compare.assert_ok(rep, f"{cfg.name} prologue {name}")
 
 
 def _check_attn(cfg, q_bits, k_bits, v_bits, out, lse, tag):
     rows = inputs.sample_rows(cfg.index, cfg.B, cfg.H, q_bits.shape[2])
-    say(f"[config {cfg.index}] oracle on {rows.size} rows ({tag})")
+    say(f"[{cfg.name}] oracle on {rows.size} rows ({tag})")
     ref_o, ref_l = oracle.attn(q_bits, k_bits, v_bits, cfg.scale, False, rows=rows)
     rep = compare.attn_report(rows_of(out, rows), ref_o, rows_of(lse, rows), ref_l,
                               bf16=out.dtype == torch.bfloat16)
-    say(f"[config {cfg.index}] {tag}: {rep}")
-    compare.assert_ok(rep, f"config {cfg.index} {tag}")
+    say(f"[{cfg.name}] {tag}: {rep}")
+    compare.assert_ok(rep, f"{cfg.name} {tag}")
 
 
-@pytest.mark.parametrize("index", [2, 3])
-def test_prologue_then_attention(index):
-    cfg = inputs.CONFIGS[index]
-    x = workload(index)
+@pytest.mark.parametrize("name", ["qwen", "cosmos"])
+def test_prologue_then_attention(name):
+    cfg = inputs.WORKLOADS[name]
+    x = workload(name)
     dq, dk, cos, sin = _prologue(cfg, x)
     _check_prologue_heads(cfg, x, dq, dk, cos, sin)
     dv = dev_bits(x["v"])
-    say(f"[config {index}] attn_fwd")
+    say(f"[{name}] attn_fwd")
     out, lse = attn_fwd(dq, dk, dv, scale=cfg.scale)
     torch.cuda.synchronize()
     _check_attn(cfg, host_bits(dq), host_bits(dk), x["v"], out, lse, "attention")
@@ -67,10 +67,10 @@ def test_prologue_then_attention(index):
 
 @pytest.mark.parametrize("times_four", [False, True], ids=["plain", "q_x4"])
 def test_wan_attention(times_four):
-    cfg = inputs.CONFIGS[4]
-    x = workload(4)
+    cfg = inputs.WORKLOADS["wan"]
+    x = workload("wan")
     qb = inputs.times_four_bits(x["q"]) if times_four else x["q"]
-    say(f"[config 4] attn_fwd {'q x4' if times_four else 'plain'}")
+    say(f"[wan] attn_fwd {'q x4' if times_four else 'plain'}")
     out, lse = attn_fwd(dev_bits(qb), dev_bits(x["k"]), dev_bits(x["v"]), scale=cfg.scale)
     torch.cuda.synchronize()
     _check_attn(cfg, qb, x["k"], x["v"], out, lse, "q x4" if times_four else "plain")
@@ -82,15 +82,15 @@ def test_wan_ring_overlap_step():
     same tensors, through the workspace path with one shared workspace), fp32
     outputs merged through their LSE.  The local window is also run through
     attn_fwd, which must give the same bits."""
-    cfg = inputs.CONFIGS[4]
-    x = workload(4)
+    cfg = inputs.WORKLOADS["wan"]
+    x = workload("wan")
     dq, dk, cos, sin = _prologue(cfg, x)
     _check_prologue_heads(cfg, x, dq, dk, cos, sin, heads=[0, 17, 39])
     dv = dev_bits(x["v"])
     c = cfg.S // 4
     ws = torch.empty((attn_fwd_workspace_bytes(cfg.B, cfg.H, cfg.S - c, cfg.D),), dtype=torch.uint8,
                      device=dq.device)
-    say("[config 4] ring-overlap attention (workspace path)")
+    say("[wan] ring-overlap attention (workspace path)")
     oa, la = attn_fwd_ws(dq, dk[:, :, :c], dv[:, :, :c], ws, scale=cfg.scale, out_dtype=torch.float32)
     op, lp = attn_fwd(dq, dk[:, :, :c], dv[:, :, :c], scale=cfg.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -102,25 +102,25 @@ def test_wan_ring_overlap_step():
     _check_attn(cfg, host_bits(dq), host_bits(dk), x["v"], oa, la, "ring-overlap step")
 
 
-@pytest.mark.parametrize("index", [2, 3])
-def test_ring_overlap_two_streams(index):
+@pytest.mark.parametrize("name", ["qwen", "cosmos"])
+def test_ring_overlap_two_streams(name):
     """Ring Attention Overlap on one GPU: the local quarter of the keys on a
     side stream, concurrently with the remote three quarters on the current
     stream, then the LSE merge.  Same bits as the one-stream order, and the
     oracle's full attention on sampled rows."""
-    cfg = inputs.CONFIGS[index]
-    x = workload(index)
+    cfg = inputs.WORKLOADS[name]
+    x = workload(name)
     dq, dk, cos, sin = _prologue(cfg, x)
     dv = dev_bits(x["v"])
     c = cfg.S // 4
     mk_ws = lambda n: torch.empty((attn_fwd_workspace_bytes(cfg.B, cfg.H, n, cfg.D),), dtype=torch.uint8,  # noqa: E731
                                   device=dq.device)
     ws_a, ws_b = mk_ws(c), mk_ws(cfg.S - c)
-    say(f"[config {index}] ring overlap, one stream")
+    say(f"[{name}] ring overlap, one stream")
     o1, l1 = attn_fwd_ring_overlap(dq, dk, dv, c, ws_a, ws_b, scale=cfg.scale)
     torch.cuda.synchronize()
     side = torch.cuda.Stream(device=dq.device)
-    say(f"[config {index}] ring overlap, two streams")
+    say(f"[{name}] ring overlap, two streams")
     o2, l2 = attn_fwd_ring_overlap(dq, dk, dv, c, ws_a, ws_b, scale=cfg.scale, side_stream=side)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
@@ -130,8 +130,8 @@ def test_ring_overlap_two_streams(index):
 
 
 def test_sp_share_chains():
-    cfg = inputs.CONFIGS[5]
-    x4 = workload(4)
+    cfg = inputs.WORKLOADS["wan_sp"]
+    x4 = workload("wan")
     q = np.ascontiguousarray(x4["q"][:, :, : cfg.Sq])
     kc, vc = inputs.split_kv(x4["k"], cfg.chunks), inputs.split_kv(x4["v"], cfg.chunks)
     dq = dev_bits(q)
@@ -139,7 +139,7 @@ def test_sp_share_chains():
     for acc_dtype in (torch.float32, torch.bfloat16):
         acc_o = acc_l = None
         for i in range(cfg.chunks):
-            say(f"[config 5] chunk {i} ({acc_dtype})")
+            say(f"[wan_sp] chunk {i} ({acc_dtype})")
             o, l = attn_fwd(dq, dev_bits(kc[i]), dev_bits(vc[i]), scale=cfg.scale, out_dtype=acc_dtype)
             if acc_o is None:
                 acc_o, acc_l = o, l
@@ -148,23 +148,23 @@ def test_sp_share_chains():
                 del o, l
         torch.cuda.synchronize()
         results[acc_dtype] = (acc_o, acc_l)
-    say("[config 5] gather path (all keys in one call)")
+    say("[wan_sp] gather path (all keys in one call)")
     go, gl = attn_fwd(dq, dev_bits(x4["k"]), dev_bits(x4["v"]), scale=cfg.scale)
     torch.cuda.synchronize()
     rows = inputs.sample_rows(cfg.index, cfg.B, cfg.H, cfg.Sq)
-    say(f"[config 5] oracle on {rows.size} rows")
+    say(f"[wan_sp] oracle on {rows.size} rows")
     ref_o, ref_l = oracle.attn(q, x4["k"], x4["v"], cfg.scale, False, rows=rows)
     reps = {}
     for name, (o, l) in (("fp32 chain", results[torch.float32]), ("bf16 chain", results[torch.bfloat16]),
                          ("gather", (go, gl))):
         reps[name] = compare.attn_report(rows_of(o, rows), ref_o, rows_of(l, rows), ref_l,
                                          bf16=o.dtype == torch.bfloat16)
-        say(f"[config 5] {name}: {reps[name]}")
+        say(f"[wan_sp] {name}: {reps[name]}")
     # The fp32 chain rounded once to bf16 at the end.
     o32 = results[torch.float32][0].to(torch.bfloat16)
     reps["fp32 chain, bf16-rounded"] = compare.attn_report(rows_of(o32, rows), ref_o)
-    say(f"[config 5] fp32 chain bf16-rounded: {reps['fp32 chain, bf16-rounded']}")
+    say(f"[wan_sp] fp32 chain bf16-rounded: {reps['fp32 chain, bf16-rounded']}")
     for name, rep in reps.items():
-        compare.assert_ok(rep, f"config 5 {name}")
+        compare.assert_ok(rep, f"wan_sp {name}")
     # Rounding every chunk to bf16 costs accuracy, as the pages warn.
     assert reps["bf16 chain"]["max_abs"] >= reps["fp32 chain"]["max_abs"]

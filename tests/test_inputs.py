@@ -24,7 +24,7 @@ def test_times_four_is_exact():
 
 
 def test_seeded_inputs_are_deterministic():
-    cfg = inputs.CONFIGS[1]
+    cfg = inputs.WORKLOADS["tiny"]
     a = inputs.make_inputs(cfg)
     b = inputs.make_inputs(cfg)
     for name in a:
@@ -34,14 +34,14 @@ def test_seeded_inputs_are_deterministic():
     assert np.all((a["w_q"] >= 0.5) & (a["w_q"] <= 1.5))
 
 
-def test_config_table_shapes():
-    c = inputs.CONFIGS
-    assert (c[2].B, c[2].H, c[2].S, c[2].D) == (1, 24, 4312, 128)
-    assert (c[3].B, c[3].H, c[3].S, c[3].D) == (2, 16, 12480, 128)
-    assert (c[4].B, c[4].H, c[4].S, c[4].D) == (1, 40, 75600, 128)
-    assert (c[5].Sq, c[5].Skv, c[5].chunks) == (18900, 75600, 4)
-    assert abs(c[4].flops() - 1.17050e14) / 1.17e14 < 1e-3
-    for i in (1, 2, 3, 4):
+def test_workload_table_shapes():
+    c = inputs.WORKLOADS
+    assert (c["qwen"].B, c["qwen"].H, c["qwen"].S, c["qwen"].D) == (1, 24, 4312, 128)
+    assert (c["cosmos"].B, c["cosmos"].H, c["cosmos"].S, c["cosmos"].D) == (2, 16, 12480, 128)
+    assert (c["wan"].B, c["wan"].H, c["wan"].S, c["wan"].D) == (1, 40, 75600, 128)
+    assert (c["wan_sp"].Sq, c["wan_sp"].Skv, c["wan_sp"].chunks) == (18900, 75600, 4)
+    assert abs(c["wan"].flops() - 1.17050e14) / 1.17e14 < 1e-3
+    for i in ("tiny", "qwen", "cosmos", "wan"):
         assert inputs.rope_positions(c[i].grid).shape[0] == c[i].S
 
 
