@@ -271,7 +271,8 @@ int attn_fwd_ws_bsnd(const void *q, const void *k, const void *v, int64_t kv_bh_
  * The bits are those of attn_fwd_ws(q, k, v, ..., tmp, tmp_lse) with an fp32
  * tmp, followed by attn_merge(out_a, lse_a, tmp, tmp_lse, ..., a_dtype,
  * DIT_FP32). Other arguments and errors are as for attn_fwd_ws, with out_a
- * in the place of out.
+ * in the place of out. As there, causal counts the keys of this chunk from
+ * 0 (j <= i); the pages' ring and sequence-parallel attention is non-causal.
  */
 int attn_fwd_ws_merge(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
                       void *workspace, int64_t workspace_bytes, void *out_a, float *lse_a,
