@@ -13,7 +13,14 @@
 //    they are copied into LDS by the buffer->LDS DMA like K (attn_fwd_ws);
 //  * otherwise each iteration loads the V tile into registers and writes it
 //    into LDS in the same image layout (attn_fwd, no workspace).
-// The 8 waves share each K/V tile in LDS.
+// The 8 waves share each K/V tile in LDS.  On the workspace path a small
+// grid with a mostly empty last round uses 4-wave workgroups (128 query
+// rows, two per CU) instead.
+//
+// Epilogue variants: rows go to BNSD or to a head slice of a BSND tensor
+// (a runtime output layout), and MERGE folds each row into a running
+// (out, lse) pair of the same queries with the arithmetic of attn_merge
+// (merge_math.h), which the ring step of the Wan2.2 page applies per chunk.
 //
 // Arithmetic design:
 //  * Scores are computed transposed, S^T = K Q^T, with
@@ -76,7 +83,8 @@ using B1 = std::integral_constant<int, 1>;
 
 constexpr int BN = 64;                 // keys per tile
 constexpr int QPW = 32;                // query rows per wave
-constexpr int WAVES = 8;               // waves per workgroup
+constexpr int WAVES = 8;               // waves per workgroup (4 for small grids, workspace path)
+constexpr int SMALL_GRID_ROUNDS = 24;  // 4-wave workgroups only below this many 8-wave rounds (256 CUs)
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float TAU = 8.0f;            // lazy-rescale threshold, log2 units
 constexpr int RSRC_WORD3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
@@ -240,19 +248,20 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run
 // slice of the softmax and the LDS fragment reads of the next chunk.  The
 // lazy O rescale of tile j is applied after P_{j-1} V_{j-1}.  One barrier
 // per tile; during sub-iteration j the DMAs of K_{j+2} and V_j are in flight.
-template <int D, bool OUT_F32, bool FQ, bool VPREP, bool MERGE = false>
-__global__ void __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64)))
+template <int D, bool OUT_F32, bool FQ, bool VPREP, bool MERGE = false, int W = WAVES>
+__global__ void __attribute__((amdgpu_flat_work_group_size(W * 64, W * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                    const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
                    float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
                    int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
                    const int* __restrict__ lkv, int out_heads, int out_h0) {
-    constexpr int BM = WAVES * QPW;
+    static_assert(W == WAVES || (W == 4 && VPREP), "4-wave workgroups read V from the workspace only");
+    constexpr int BM = W * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int TILE = BN * D;                         // elements of one K or V tile
-    constexpr int KDMA = TILE * 2 / 1024 / WAVES;     // 1 KB DMA chunks per wave per tile
-    static_assert(KDMA >= 1 && KDMA * WAVES * 1024 == TILE * 2, "tile shape");
+    constexpr int KDMA = TILE * 2 / 1024 / W;         // 1 KB DMA chunks per wave per tile
+    static_assert(KDMA >= 1 && KDMA * W * 1024 == TILE * 2, "tile shape");
 
     __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
@@ -378,7 +387,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     // given d fill a whole 128-byte image row.
     constexpr int VDC = D / 8;                        // d-chunks per key row
     const int v_kp = lane & 31, v_dc = (wave * 64 + lane) >> 5;
-    const bool v_on = VDC * 32 == WAVES * 64 || v_dc < VDC;   // every thread when D = 128
+    const bool v_on = VDC * 32 == W * 64 || v_dc < VDC;       // every thread when D = 128
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(v + (int64_t)bkv * kv_bh_stride), (short)0, VPREP ? 0 : Skv * D * 2, RSRC_WORD3);
     u32x4 vst[2];
@@ -519,8 +528,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     dma_k(0, B0{});
     dma_k(BN, B1{});
 #pragma unroll
-    for (int i = 0; i < TILE / (WAVES * 512); ++i)
-        *(u32x4*)(Vt1 + (i * WAVES * 64 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < TILE / (W * 512); ++i)
+        *(u32x4*)(Vt1 + (i * W * 64 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -573,25 +582,35 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
                   int BH, int H, int G, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
                   const QNormRope* qn, const int* lq, const int* lkv, int out_heads, int out_h0, bool merge,
                   hipStream_t stream) {
-    constexpr int BM = WAVES * QPW;
-    const int n_qtiles = (Sq + BM - 1) / BM;
-    const int64_t nblk = (int64_t)n_qtiles * BH;
-    if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
     const QNormRope qz{};
-    auto go = [&](auto kern, const QNormRope& qa) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(WAVES * 64), 0, stream, (const uint16_t*)q,
+    // Workspace path on a small grid whose last round of 8-wave workgroups
+    // over 256 CUs is at most half full: 4-wave workgroups of 128 query rows,
+    // two per CU.  The per-row arithmetic is the same.  In the last round
+    // each CU then holds at most one of them, and a lone 4-wave workgroup
+    // runs faster; elsewhere 8-wave workgroups are a little faster.
+    const int64_t blk8 = (int64_t)((Sq + WAVES * QPW - 1) / (WAVES * QPW)) * BH;
+    const int64_t tail8 = blk8 % 256;
+    const bool small = vws != nullptr && blk8 < (int64_t)SMALL_GRID_ROUNDS * 256 && tail8 > 0 && tail8 <= 128;
+    auto go = [&](auto kern, const QNormRope& qa, int w) -> hipError_t {
+        const int bm = w * QPW;
+        const int n_qtiles = (Sq + bm - 1) / bm;
+        const int64_t nblk = (int64_t)n_qtiles * BH;
+        if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(w * 64), 0, stream, (const uint16_t*)q,
                            (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)vws, kv_bh_stride, out, lse, Sq,
                            Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, qa, lq, lkv, out_heads, out_h0);
+        return hipGetLastError();
     };
     if (merge)
-        go(attn_fwd_kernel<D, OUT_F32, false, true, true>, qz);
-    else if (vws && qn)
-        go(attn_fwd_kernel<D, OUT_F32, true, true>, *qn);
-    else if (vws)
-        go(attn_fwd_kernel<D, OUT_F32, false, true>, qz);
-    else
-        go(attn_fwd_kernel<D, OUT_F32, false, false>, qz);
-    return hipGetLastError();
+        return small ? go(attn_fwd_kernel<D, OUT_F32, false, true, true, 4>, qz, 4)
+                     : go(attn_fwd_kernel<D, OUT_F32, false, true, true>, qz, WAVES);
+    if (vws && qn)
+        return small ? go(attn_fwd_kernel<D, OUT_F32, true, true, false, 4>, *qn, 4)
+                     : go(attn_fwd_kernel<D, OUT_F32, true, true>, *qn, WAVES);
+    if (vws)
+        return small ? go(attn_fwd_kernel<D, OUT_F32, false, true, false, 4>, qz, 4)
+                     : go(attn_fwd_kernel<D, OUT_F32, false, true>, qz, WAVES);
+    return go(attn_fwd_kernel<D, OUT_F32, false, false>, qz, WAVES);
 }
 
 }  // namespace

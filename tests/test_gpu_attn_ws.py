@@ -108,3 +108,30 @@ def test_value_range_of_v():
     assert np.all(np.isfinite(got))
     assert float(np.max(np.abs(got - ref_o))) <= 2.0 ** -10 * vmax
     assert float(np.max(np.abs(host_f64(l1) - ref_l))) <= 1e-3
+
+
+@pytest.mark.parametrize("B,H,Sq,causal", [
+    (1, 129, 256, False),     # 129 workgroups of 256 rows: last round more than half full, 8-wave workgroups
+    (1, 128, 256, True),      # 128: at most half full, 4-wave workgroups of 128 rows
+    (3, 43, 300, False),      # 258 = one full round + 2: 4-wave workgroups
+    (2, 100, 200, False),     # 200: 8-wave workgroups
+])
+def test_ws_workgroup_sizes_match_plain(B, H, Sq, causal):
+    """The workspace path launches 8- or 4-wave workgroups depending on the
+    grid; both give the bits of the path without a workspace (always 8-wave
+    workgroups) and agree with the oracle on sampled rows."""
+    Skv, D = 150, 128
+    q = inputs.random_bits(B * H + Sq, (B, H, Sq, D))
+    k = inputs.random_bits(B * H + Sq + 1, (B, H, Skv, D))
+    v = inputs.random_bits(B * H + Sq + 2, (B, H, Skv, D))
+    say(f"[ws] workgroup sizes B{B} H{H} Sq{Sq} causal={causal}")
+    dq, dk, dv = dev_bits(q), dev_bits(k), dev_bits(v)
+    o_ws, l_ws = attn_fwd_ws(dq, dk, dv, _ws(B, H, Skv, D), causal=causal, out_dtype=torch.float32)
+    o_pl, l_pl = attn_fwd(dq, dk, dv, causal=causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o_ws, o_pl) and torch.equal(l_ws, l_pl)
+    rows = np.random.default_rng(Sq).choice(B * H * Sq, 300, replace=False)
+    ref_o, ref_l = oracle.attn(q, k, v, 1 / math.sqrt(D), causal, rows=rows)
+    got_o = host_f64(o_ws).reshape(-1, D)[rows]
+    got_l = host_f64(l_ws).reshape(-1)[rows]
+    compare.assert_ok(compare.attn_report(got_o, ref_o, got_l, ref_l, bf16=False), "workgroup sizes")
