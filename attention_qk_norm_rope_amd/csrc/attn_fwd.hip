@@ -13,9 +13,9 @@
 //    they are copied into LDS by the buffer->LDS DMA like K (attn_fwd_ws);
 //  * otherwise each iteration loads the V tile into registers and writes it
 //    into LDS in the same image layout (attn_fwd, no workspace).
-// The 8 waves share each K/V tile in LDS.  On the workspace path a small
-// grid with a mostly empty last round uses 4-wave workgroups (128 query
-// rows, two per CU) instead.
+// The 8 waves share each K/V tile in LDS.  On the workspace path, a last
+// round of workgroups that would leave most CUs idle runs as 4-wave
+// workgroups of 128 query rows instead.
 //
 // Epilogue variants: rows go to BNSD or to a head slice of a BSND tensor
 // (a runtime output layout), and MERGE folds each row into a running
@@ -84,7 +84,7 @@ using B1 = std::integral_constant<int, 1>;
 constexpr int BN = 64;                 // keys per tile
 constexpr int QPW = 32;                // query rows per wave
 constexpr int WAVES = 8;               // waves per workgroup (4 for small grids, workspace path)
-constexpr int SMALL_GRID_ROUNDS = 24;  // 4-wave workgroups only below this many 8-wave rounds (256 CUs)
+constexpr int SMALL_GRID_ROUNDS = 24;  // causal grids: 4-wave workgroups only below this many 8-wave rounds
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float TAU = 8.0f;            // lazy-rescale threshold, log2 units
 constexpr int RSRC_WORD3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
@@ -255,7 +255,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
                    const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
                    float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
                    int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
-                   const int* __restrict__ lkv, int out_heads, int out_h0) {
+                   const int* __restrict__ lkv, int out_heads, int out_h0, int tile0, int halves) {
     static_assert(W == WAVES || (W == 4 && VPREP), "4-wave workgroups read V from the workspace only");
     constexpr int BM = W * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
@@ -270,7 +270,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     auto Kbuf = [&](auto bc) -> uint16_t* { if constexpr (decltype(bc)::value == 0) return Ks0; else return Ks1; };
     auto Vbuf = [&](auto bc) -> uint16_t* { if constexpr (decltype(bc)::value == 0) return Vt0; else return Vt1; };
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    // Tile of this workgroup: logical tile tile0 + id of n_qtiles tiles per
+    // head; with halves, two consecutive workgroups split one tile of 2*BM
+    // rows (the tail of a grid of larger workgroups).
+    int logical = xcd_remap(blockIdx.x, gridDim.x);
+    int half = 0;
+    if (halves) {
+        half = logical & 1;
+        logical >>= 1;
+    }
+    logical += tile0;
     const int bh = logical / n_qtiles;
     const int bkv = kv_head(bh, H, G);
     // Per-batch valid lengths (variable-length batches): query rows >= Sq_b
@@ -279,7 +288,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     const int Skv = lkv ? min(max(lkv[bh / H], 0), Skv_all) : Skv_all;
     int qt = logical - bh * n_qtiles;
     if (causal) qt = n_qtiles - 1 - qt;
-    const int q0 = qt * BM;
+    const int q0 = halves ? (2 * qt + half) * BM : qt * BM;
 
     const int tid = threadIdx.x;
     // wave is uniform: kept scalar so the DMA's LDS address (M0) needs no VALU.
@@ -583,34 +592,47 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
                   const QNormRope* qn, const int* lq, const int* lkv, int out_heads, int out_h0, bool merge,
                   hipStream_t stream) {
     const QNormRope qz{};
-    // Workspace path on a small grid whose last round of 8-wave workgroups
-    // over 256 CUs is at most half full: 4-wave workgroups of 128 query rows,
-    // two per CU.  The per-row arithmetic is the same.  In the last round
-    // each CU then holds at most one of them, and a lone 4-wave workgroup
-    // runs faster; elsewhere 8-wave workgroups are a little faster.
-    const int64_t blk8 = (int64_t)((Sq + WAVES * QPW - 1) / (WAVES * QPW)) * BH;
-    const int64_t tail8 = blk8 % 256;
-    const bool small = vws != nullptr && blk8 < (int64_t)SMALL_GRID_ROUNDS * 256 && tail8 > 0 && tail8 <= 128;
-    auto go = [&](auto kern, const QNormRope& qa, int w) -> hipError_t {
-        const int bm = w * QPW;
-        const int n_qtiles = (Sq + bm - 1) / bm;
-        const int64_t nblk = (int64_t)n_qtiles * BH;
-        if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // One launch of workgroups of w waves over tiles [tile0, tile0 + ntile)
+    // of n_qtiles per head; with halves, every tile of 2*w*QPW rows goes to
+    // two workgroups.
+    auto go = [&](auto kern, const QNormRope& qa, int w, int n_qtiles, int64_t tile0, int64_t ntile,
+                  bool halves) -> hipError_t {
+        const int64_t nblk = halves ? 2 * ntile : ntile;
+        if (nblk > 0x7FFFFFFF || tile0 + ntile > 0x7FFFFFFF) return hipErrorInvalidValue;
+        if (nblk == 0) return hipSuccess;
         hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(w * 64), 0, stream, (const uint16_t*)q,
                            (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)vws, kv_bh_stride, out, lse, Sq,
-                           Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, qa, lq, lkv, out_heads, out_h0);
+                           Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, qa, lq, lkv, out_heads, out_h0,
+                           (int)tile0, halves ? 1 : 0);
         return hipGetLastError();
     };
+    const int nq8 = (Sq + WAVES * QPW - 1) / (WAVES * QPW);
+    const int64_t blk8 = (int64_t)nq8 * BH;
+    const int64_t tail8 = blk8 % 256, full8 = blk8 - tail8;
+    // Workspace path: when the last round of 8-wave workgroups over 256 CUs
+    // is at most half full, those tiles run as twice as many 4-wave
+    // workgroups of 128 query rows in a second launch.  Each CU then holds at
+    // most one of them, and a lone 4-wave workgroup runs faster than an
+    // 8-wave one.  The per-row arithmetic is the same.  Causal grids, whose
+    // tiles differ in cost, use 4-wave workgroups throughout when the grid
+    // is small.
+    const bool tail_split = vws != nullptr && !causal && tail8 > 0 && tail8 <= 128;
+    const bool all4 = vws != nullptr && causal && blk8 < (int64_t)SMALL_GRID_ROUNDS * 256 && tail8 > 0 && tail8 <= 128;
+    auto run = [&](auto k8, auto k4, const QNormRope& qa) -> hipError_t {
+        if (all4) return go(k4, qa, 4, (Sq + 4 * QPW - 1) / (4 * QPW), 0, (int64_t)((Sq + 4 * QPW - 1) / (4 * QPW)) * BH,
+                            false);
+        if (!tail_split) return go(k8, qa, WAVES, nq8, 0, blk8, false);
+        const hipError_t e = go(k8, qa, WAVES, nq8, 0, full8, false);
+        if (e != hipSuccess) return e;
+        return go(k4, qa, 4, nq8, full8, tail8, true);
+    };
     if (merge)
-        return small ? go(attn_fwd_kernel<D, OUT_F32, false, true, true, 4>, qz, 4)
-                     : go(attn_fwd_kernel<D, OUT_F32, false, true, true>, qz, WAVES);
+        return run(attn_fwd_kernel<D, OUT_F32, false, true, true>, attn_fwd_kernel<D, OUT_F32, false, true, true, 4>, qz);
     if (vws && qn)
-        return small ? go(attn_fwd_kernel<D, OUT_F32, true, true, false, 4>, *qn, 4)
-                     : go(attn_fwd_kernel<D, OUT_F32, true, true>, *qn, WAVES);
+        return run(attn_fwd_kernel<D, OUT_F32, true, true>, attn_fwd_kernel<D, OUT_F32, true, true, false, 4>, *qn);
     if (vws)
-        return small ? go(attn_fwd_kernel<D, OUT_F32, false, true, false, 4>, qz, 4)
-                     : go(attn_fwd_kernel<D, OUT_F32, false, true>, qz, WAVES);
-    return go(attn_fwd_kernel<D, OUT_F32, false, false>, qz, WAVES);
+        return run(attn_fwd_kernel<D, OUT_F32, false, true>, attn_fwd_kernel<D, OUT_F32, false, true, false, 4>, qz);
+    return go(attn_fwd_kernel<D, OUT_F32, false, false>, qz, WAVES, nq8, 0, blk8, false);
 }
 
 }  // namespace

@@ -111,15 +111,17 @@ def test_value_range_of_v():
 
 
 @pytest.mark.parametrize("B,H,Sq,causal", [
-    (1, 129, 256, False),     # 129 workgroups of 256 rows: last round more than half full, 8-wave workgroups
-    (1, 128, 256, True),      # 128: at most half full, 4-wave workgroups of 128 rows
-    (3, 43, 300, False),      # 258 = one full round + 2: 4-wave workgroups
-    (2, 100, 200, False),     # 200: 8-wave workgroups
+    (1, 129, 256, False),     # 129 tiles of 256 rows: last round more than half full, one 8-wave launch
+    (1, 128, 256, True),      # causal, small grid, last round half full: 4-wave workgroups throughout
+    (3, 43, 300, False),      # 258 tiles = one full round + 2: 8-wave launch, then the 2 tiles as 4 halves
+    (1, 96, 256, False),      # 96 tiles, no full round: the halves launch alone
+    (2, 100, 200, False),     # 200 tiles: one 8-wave launch
 ])
 def test_ws_workgroup_sizes_match_plain(B, H, Sq, causal):
-    """The workspace path launches 8- or 4-wave workgroups depending on the
-    grid; both give the bits of the path without a workspace (always 8-wave
-    workgroups) and agree with the oracle on sampled rows."""
+    """The workspace path launches 8-wave workgroups, 4-wave workgroups, or
+    8-wave workgroups followed by the last round's tiles as 4-wave halves,
+    depending on the grid; every form gives the bits of the path without a
+    workspace (one 8-wave launch) and agrees with the oracle on sampled rows."""
     Skv, D = 150, 128
     q = inputs.random_bits(B * H + Sq, (B, H, Sq, D))
     k = inputs.random_bits(B * H + Sq + 1, (B, H, Skv, D))
