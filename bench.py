@@ -397,10 +397,12 @@ def main():
     if "attn_fwd" in per_kernel:
         attn_ms_total = sum(per_kernel["attn_fwd"]) / args.steps          # per step
         n_attn = launches["attn_fwd"]
-        entry = "attn_fwd_ws (v_prep_kernel + attn_fwd_kernel per call)"
+        entry = ("attn_fwd_ws (per call: v_prep_kernel, then attn_fwd_kernel; a last round that would fill at "
+                 "most half the CUs runs as a second dispatch of 4-wave workgroups)")
         if wl in ("wan", "sp") and args.fuse_merge:
-            entry = ("attn_fwd_ws + attn_fwd_ws_merge (v_prep_kernel + attn_fwd_kernel per call; the second "
-                     "merges into the first's output in its epilogue)")
+            entry = ("attn_fwd_ws + attn_fwd_ws_merge (per call: v_prep_kernel, then attn_fwd_kernel; a last round "
+                     "that would fill at most half the CUs runs as a second dispatch of 4-wave workgroups; the "
+                     "second call merges into the first's output in its epilogue)")
     else:
         # Two streams: the interval spans both overlapped calls and the merge.
         attn_ms_total = sum(per_kernel["attn_fwd+attn_merge"]) / args.steps
