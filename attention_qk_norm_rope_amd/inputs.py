@@ -222,16 +222,19 @@ def config_rope_tables(cfg: Config):
 # --------------------------------------------------------------------------
 # Query-row sample for the oracle at large sizes
 
-def sample_rows(cfg_index: int, B: int, H: int, Sq: int, per_head: int = 64) -> np.ndarray:
+def sample_rows(cfg_index: int, B: int, H: int, Sq: int, per_head: int = 64, extra=()) -> np.ndarray:
     """Flat query-row ids ((b*H + h)*Sq + i) the oracle evaluates.
 
-    Per (b, h): rows 0, 127, 128, the last 16 rows (the ragged tail) and
-    Sq - 1, topped up to ``per_head`` distinct rows drawn uniformly from
-    ``default_rng(100 + cfg_index)``.
+    Per (b, h): rows 0, 31, 32, 127, 128, 255, 256 (edges of 32-, 128- and
+    256-row query blocks), the last 16 rows (the ragged tail) and Sq - 1,
+    topped up to ``per_head`` distinct rows drawn uniformly from
+    ``default_rng(100 + cfg_index)``.  ``extra`` flat row ids are added on
+    top (sorted, without duplicates).
     """
     rng = np.random.default_rng(100 + cfg_index)
     rows = []
-    fixed = sorted({i for i in [0, 127, 128, Sq - 1] + list(range(max(0, Sq - 16), Sq)) if 0 <= i < Sq})
+    fixed = sorted({i for i in [0, 31, 32, 127, 128, 255, 256, Sq - 1] + list(range(max(0, Sq - 16), Sq))
+                    if 0 <= i < Sq})
     for bh in range(B * H):
         chosen = set(fixed)
         want = min(per_head, Sq)
@@ -239,4 +242,7 @@ def sample_rows(cfg_index: int, B: int, H: int, Sq: int, per_head: int = 64) -> 
             chosen.update(int(x) for x in rng.integers(0, Sq, size=want - len(chosen)))
         sel = sorted(chosen)[:want] if len(chosen) > want else sorted(chosen)
         rows.extend(bh * Sq + i for i in sel)
+    if len(extra):
+        ex = [int(r) for r in extra if 0 <= int(r) < B * H * Sq]
+        rows = sorted(set(rows) | set(ex))
     return np.asarray(rows, dtype=np.int64)

@@ -50,7 +50,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    # A library older than its source would check against stale arithmetic.
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         build()
     lib = ctypes.CDLL(_LIB)
     p = ctypes.c_void_p
@@ -182,8 +183,10 @@ def bnsd_to_bsnd(o, x, h0: int = 0):
 def attn_varlen(q, k, v, seqlens_q, seqlens_kv, scale: float, causal: bool = False):
     """Attention over padded batches, from the definition: batch b is full
     attention of its first seqlens_q[b] query rows over its first
-    seqlens_kv[b] keys (K/V head h // (H // Hkv) for query head h); padding
-    rows, and rows that see no key, are 0 with LSE -inf.  q [B,H,Sq,D], k, v
+    seqlens_kv[b] keys (K/V head h // (H // Hkv) for query head h: H/Hkv
+    consecutive query heads share one K/V head, the grouping of the fused
+    attention's num_key_value_heads on the Wan2.2 NPU page); padding rows,
+    and rows that see no key, are 0 with LSE -inf.  q [B,H,Sq,D], k, v
     [B,Hkv,Skv,D] bf16 bits.  Returns fp64 out [B,H,Sq,D], lse [B,H,Sq]."""
     q, k, v = _bits(q, "q"), _bits(k, "k"), _bits(v, "v")
     B, H, Sq, D = q.shape

@@ -269,8 +269,10 @@ int oracle_qk_norm_rope(const uint16_t *x, const float *w, const float *cos_t,
  * and B:
  *   M = max(la, lb),  L = M + ln(exp(la - M) + exp(lb - M))
  *   O = exp(la - L) O_a + exp(lb - L) O_b
- * which equals the attention over A u B.  When both la and lb are -inf the
- * row saw no key: O = 0 and L = -inf.
+ * which equals the attention over A u B.  A side whose LSE is -inf is the
+ * attention over an empty key set (ln of an empty sum): it holds no key, so
+ * it adds no term at all, whatever its output values are.  When both la and
+ * lb are -inf the row saw no key: O = 0 and L = -inf.
  */
 int oracle_merge(const double *out_a, const double *lse_a, const double *out_b,
                  const double *lse_b, int64_t rows, int D, double *out, double *lse)
@@ -289,10 +291,17 @@ int oracle_merge(const double *out_a, const double *lse_a, const double *out_b,
             lse[r] = -INFINITY;
             continue;
         }
+        int has_a = la != -INFINITY, has_b = lb != -INFINITY;
         double L = M + log(exp(la - M) + exp(lb - M));
         double wa = exp(la - L), wb = exp(lb - L);
-        for (int d = 0; d < D; ++d)
-            o[d] = wa * oa[d] + wb * ob[d];
+        for (int d = 0; d < D; ++d) {
+            double x = 0.0;
+            if (has_a)
+                x += wa * oa[d];
+            if (has_b)
+                x += wb * ob[d];
+            o[d] = x;
+        }
         lse[r] = L;
     }
     return 0;

@@ -147,4 +147,7 @@ def test_merge_ignores_the_empty_side():
     ob = torch.randn(B, H, Sq, D, device="cuda")
     lb = torch.randn(B, H, Sq, device="cuda")
     attn_merge(oa, la, ob, lb)
+    ref_o, ref_l = oracle.merge(np.full((Sq, D), np.nan), np.full(Sq, -np.inf), host_f64(ob).reshape(Sq, D),
+                                host_f64(lb).reshape(Sq))
+    assert np.array_equal(host_f64(oa).reshape(Sq, D), ref_o) and np.array_equal(host_f64(la).reshape(Sq), ref_l)
     assert torch.equal(oa, ob) and torch.equal(la, lb)

@@ -66,5 +66,13 @@ def test_ws_merge_into_empty_side(a_dtype):
     attn_fwd_ws_merge(dq, dk, dv, ws, oa, la)
     o1, l1 = attn_fwd_ws(dq, dk, dv, ws, out_dtype=a_dtype)
     torch.cuda.synchronize()
+    # The oracle's merge of an empty running side with this chunk's result.
+    rows = B * H * Sq
+    ref_o, ref_l = oracle.merge(np.full((rows, D), np.nan), np.full(rows, -np.inf),
+                                host_f64(o1).reshape(rows, D), host_f64(l1).reshape(rows))
+    assert np.array_equal(host_f64(oa).reshape(rows, D), ref_o) and np.array_equal(host_f64(la).reshape(rows), ref_l)
     assert torch.equal(oa, o1) and torch.equal(la, l1)
     assert np.isfinite(host_f64(oa)).all()
+    full_o, full_l = oracle.attn(q, k, v, 1 / math.sqrt(D), False)
+    rep = compare.attn_report(host_f64(oa), full_o, host_f64(la), full_l, bf16=a_dtype == torch.bfloat16)
+    compare.assert_ok(rep, "ws merge into an empty running side")

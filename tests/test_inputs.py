@@ -71,8 +71,12 @@ def test_sample_rows():
     per = rows.reshape(3, 64) - (np.arange(3) * 300)[:, None]
     for r in per:
         assert len(set(r.tolist())) == 64
-        assert {0, 127, 128, 299, 284}.issubset(set(r.tolist()))
+        assert {0, 31, 32, 127, 128, 255, 256, 299, 284}.issubset(set(r.tolist()))
         assert r.min() >= 0 and r.max() < 300
     np.testing.assert_array_equal(rows, inputs.sample_rows(2, 1, 3, 300, per_head=64))
     small = inputs.sample_rows(1, 1, 1, 10, per_head=64)
     np.testing.assert_array_equal(small, np.arange(10))
+    # extra flat rows are added on top, once, in order; out-of-range ids are dropped
+    more = inputs.sample_rows(2, 1, 3, 300, per_head=64, extra=[450, 450, 0, 10 ** 6])
+    assert set(more.tolist()) == set(rows.tolist()) | {450}
+    assert np.all(np.diff(more) > 0)

@@ -1,6 +1,7 @@
 """Pins for the fp64 out/LSE merge oracle (CPU only).
 
-Checks: a pair worked by hand; identity when one side saw no key; the
+Checks: a pair worked by hand; identity when one side saw no key, also
+when that side's values are NaN (an empty key set adds no term); the
 empty/empty case; commutativity and associativity; equal LSE gives the
 average; merged chunk attentions from torch's SDPA (library, float64) equal
 torch's full attention; and the negative case of the ring bug on the pages
@@ -43,6 +44,24 @@ def test_empty_side_is_identity(oracle):
     np.testing.assert_array_equal(o, oa)
     np.testing.assert_array_equal(l, la)
     o, l = oracle.merge(oa, ninf, ob, ninf)
+    np.testing.assert_array_equal(o, 0.0)
+    assert np.all(l == -np.inf)
+
+
+def test_empty_side_adds_no_term_even_with_nan_values(oracle):
+    """The merge is the attention over the union of two key sets.  A side
+    with LSE -inf is the attention over an empty key set: it holds no key, so
+    whatever its output buffer contains (NaN here) it adds no term."""
+    oa, la = _rand(11, 6, 8)
+    nan = np.full((6, 8), np.nan)
+    ninf = np.full(6, -np.inf)
+    o, l = oracle.merge(nan, ninf, oa, la)
+    np.testing.assert_array_equal(o, oa)
+    np.testing.assert_array_equal(l, la)
+    o, l = oracle.merge(oa, la, nan, ninf)
+    np.testing.assert_array_equal(o, oa)
+    np.testing.assert_array_equal(l, la)
+    o, l = oracle.merge(nan, ninf, nan, ninf)
     np.testing.assert_array_equal(o, 0.0)
     assert np.all(l == -np.inf)
 
