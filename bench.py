@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the DiT attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan|qwen|cosmos|sp]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan|qwen|cosmos|sp|ulysses]
+                    [--no-cpu-baseline] [--no-configs]
 
 One step is one pass of the whole path over one batch of synthetic input.
 Default workload (Wan2.2 shape, B1 H40 S75600 D128, bf16 ~ N(0,1)), laid out
@@ -22,8 +22,17 @@ inside the timed interval of the call.
 
 `value` is that attention FLOP count divided by the whole step's time
 (TFLOP/s).  Kernel durations come from HIP events recorded on the stream the
-kernels are launched on (torch's current stream).  The CPU baseline times the
-fp64 oracle on a bounded sample of query rows on the host cores.
+kernels are launched on (torch's current stream); mean, median and min are
+reported, with the engine clock and socket power sampled during the timed
+steps.  The CPU baseline times the fp64 oracle on this process's CPU share:
+attention on 64 sampled query rows per head (extrapolated to every row), the
+prologue of q and k in full (also compared element by element with the GPU
+prologue) and a merge of the step's full shape.
+
+After the default step, the line's "configs" key reports the other
+workloads, each timed in the same run and compared with the oracle on its
+sampled rows: Wan2.2 with q x4 (logit std ~4), the 4-way SP share, Qwen-Image
+and Cosmos-Predict (--no-configs skips them).
 
 Other workloads (--workload) are per-config measurements:
   qwen / cosmos: prologue (out of place), attn_fwd_ws over all keys;
@@ -61,6 +70,9 @@ def parse():
                     help="ulysses: only the BSND<->BNSD head-slice layout kernels of one rank of a 4-way "
                          "Ulysses split at the Wan2.2 shape (reported in GB/s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="wan workload: skip the timed runs of the other workloads (Wan2.2 Q x4, the SP share, "
+                         "Qwen-Image, Cosmos-Predict) that the default line reports under 'configs'")
     ap.add_argument("--fuse-q", action="store_true",
                     help="wan workload: apply the query RMSNorm+RoPE inside the attention's Q load "
                          "(attn_fwd_ws_fused_q); the prologue kernel then normalises k only")
@@ -194,6 +206,310 @@ def bench_ulysses(args):
     }), flush=True)
 
 
+def _stats(ts) -> dict:
+    """Mean, median and min of a list of durations (ms)."""
+    ts = sorted(float(t) for t in ts)
+    n = len(ts)
+    med = ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
+    return {"mean": sum(ts) / n, "median": med, "min": ts[0]}
+
+
+class ClockSampler:
+    """Reads the GPU engine (GFX) clock through amdsmi on a host thread while
+    the timed steps run, so the line states the clock the kernels ran at (the
+    card lowers it under its power limit)."""
+
+    def __init__(self, period_s: float = 0.02):
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = None
+        self._thread = None
+        self._read = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def read():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                clks = [c for c in m["current_gfxclks"] if isinstance(c, (int, float))]
+                return (sum(clks) / len(clks), float(m["current_socket_power"]))
+
+            self._read = read
+            self._read()
+        except Exception as e:  # noqa: BLE001 - the clock is reported as unavailable
+            self.error = f"amdsmi unavailable: {e!r}"
+            self._read = None
+
+    def start(self):
+        if self._read is None:
+            return
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception as e:  # noqa: BLE001
+                    self.error = repr(e)
+                    return
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def stop(self) -> dict:
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if not self.samples:
+            return {"source": "amdsmi GFX clock", "error": self.error or "no samples"}
+        clk = _stats([c for c, _ in self.samples])
+        pw = _stats([p for _, p in self.samples])
+        return {"source": "amdsmi GPU metrics (engine clock averaged over the XCDs, socket power), sampled "
+                          "every 20 ms during the timed steps",
+                "median_mhz": round(clk["median"]), "min_mhz": round(clk["min"]),
+                "max_mhz": round(max(c for c, _ in self.samples)), "median_socket_w": round(pw["median"]),
+                "samples": len(self.samples)}
+
+
+def _time_calls(fn, warmup: int, reps: int, n_marks: int):
+    """Run fn(events) warmup + reps times; fn records n_marks + 1 HIP events
+    on the current stream.  Returns, per interval, the list of the reps'
+    durations (ms)."""
+    import torch
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_marks + 1)]  # noqa: E731
+    for _ in range(warmup):
+        fn(mk())
+    evs = [mk() for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        fn(e)
+    torch.cuda.synchronize()
+    return [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(n_marks)]
+
+
+def _attn_entry(name, ms_list, flop, extra=None) -> dict:
+    st = _stats(ms_list)
+    r = {"entry": name, "avg_ms": round(st["mean"], 4), "median_ms": round(st["median"], 4),
+         "min_ms": round(st["min"], 4), "flop": flop,
+         "tflops": round(flop / (st["median"] * 1e-3) / 1e12, 2),
+         "frac_bf16_peak": round(flop / (st["median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if extra:
+        r.update(extra)
+    return r
+
+
+def _bw_entry(ms_list, nbytes) -> dict:
+    st = _stats(ms_list)
+    gbs = nbytes / (st["median"] * 1e-3) / 1e9
+    return {"avg_ms": round(st["mean"], 4), "median_ms": round(st["median"], 4), "min_ms": round(st["min"], 4),
+            "bytes": nbytes, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def _match(final_out, final_lse, rows, ref_o, ref_l, D):
+    import torch
+    from oracle import compare
+    idx = torch.from_numpy(rows).to(final_out.device)
+    got_o = final_out.reshape(-1, D).index_select(0, idx).double().cpu().numpy()
+    got_l = final_lse.reshape(-1).index_select(0, idx).double().cpu().numpy()
+    rep = compare.attn_report(got_o, ref_o, got_l, ref_l, bf16=final_out.dtype == torch.bfloat16)
+    rep["rows"] = int(rows.size)
+    return {k: (round(v, 8) if isinstance(v, float) else v) for k, v in rep.items()}
+
+
+def run_configs(args, dev, wan) -> dict:
+    """Attention of the other workloads, timed in the same run (HIP events on
+    the current stream; median and min over the reps) and each compared with
+    the oracle on its sampled rows."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from attention_qk_norm_rope_amd import (attn_fwd_workspace_bytes, attn_fwd_ws, attn_fwd_ws_merge, inputs,
+                                            qk_norm_rope_out)
+    res = {}
+    bits = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+
+    # Wan2.2 Q x4: the normalised q times 4 (exact in bf16) through the same
+    # two calls as the default step: logit std about 4.
+    cfg = wan["cfg"]
+    B, H, S, D = cfg.B, cfg.H, cfg.S, cfg.D
+    c = S // 4
+    q4 = wan["q"] * 4
+    out = torch.empty((B, H, S, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    k, v, ws = wan["k"], wan["v"], wan["ws"]
+
+    def wan_q4(e):
+        e[0].record()
+        attn_fwd_ws(q4, k[:, :, :c], v[:, :, :c], ws, out=out, lse=lse, scale=cfg.scale)
+        attn_fwd_ws_merge(q4, k[:, :, c:], v[:, :, c:], ws, out, lse, scale=cfg.scale)
+        e[1].record()
+
+    log("[bench] configs: wan q x4")
+    (t_att,) = _time_calls(wan_q4, 2, 5, 1)
+    r = _attn_entry("attn_fwd_ws + attn_fwd_ws_merge (local 1/4 + remote 3/4 of the keys)", t_att, cfg.flops(),
+                    {"workload": "Wan2.2 B1 H40 S75600 D128, normalised q x4 (logit std ~4)"})
+    if not args.no_cpu_baseline:
+        rows = inputs.sample_rows(cfg.index, B, H, S, per_head=64)
+        ref_o, ref_l = oracle.attn(bits(q4), bits(k), wan["v_bits"], cfg.scale, False, rows=rows)
+        r["oracle_match"] = _match(out, lse, rows, ref_o, ref_l, D)
+    res["wan_q4"] = r
+    del q4
+
+    # One GPU's share of 4-way sequence parallelism: 4 KV chunks folded into
+    # an fp32 (out, lse) in the attention epilogue.
+    sp = inputs.WORKLOADS["wan_sp"]
+    n, cs = sp.chunks, sp.Skv // sp.chunks
+    qs = wan["q0"][:, :, :sp.Sq].contiguous()
+    k0 = wan["k0"]
+    outs = torch.empty((B, H, sp.Sq, D), dtype=torch.float32, device=dev)
+    lses = torch.empty((B, H, sp.Sq), dtype=torch.float32, device=dev)
+
+    def sp_step(e):
+        e[0].record()
+        for i in range(n):
+            kc, vc = k0[:, :, i * cs:(i + 1) * cs], v[:, :, i * cs:(i + 1) * cs]
+            if i == 0:
+                attn_fwd_ws(qs, kc, vc, ws, out=outs, lse=lses, scale=sp.scale)
+            else:
+                attn_fwd_ws_merge(qs, kc, vc, ws, outs, lses, scale=sp.scale)
+        e[1].record()
+
+    log("[bench] configs: sp share")
+    (t_att,) = _time_calls(sp_step, 2, 10, 1)
+    r = _attn_entry("attn_fwd_ws + 3 x attn_fwd_ws_merge (4 KV chunks of 18900 keys, fp32 accumulator)", t_att,
+                    sp.flops(), {"workload": "Wan2.2 4-way SP share: Sq 18900 x Skv 75600, H40 D128"})
+    if not args.no_cpu_baseline:
+        rows = inputs.sample_rows(sp.index, B, H, sp.Sq, per_head=64)
+        qs_bits = np.ascontiguousarray(wan["q0_bits"][:, :, :sp.Sq])
+        ref_o, ref_l = oracle.attn(qs_bits, wan["k0_bits"], wan["v_bits"], sp.scale, False, rows=rows)
+        r["oracle_match"] = _match(outs, lses, rows, ref_o, ref_l, D)
+    res["sp"] = r
+    del outs, lses
+
+    # Qwen-Image and Cosmos-Predict: prologue, then attention over all keys.
+    to_dev = wan["to_dev"]
+    for name, reps in (("qwen", 50), ("cosmos", 20)):
+        cf = inputs.WORKLOADS[name]
+        log(f"[bench] configs: {name}")
+        x = inputs.make_inputs(cf)
+        cos, sin = inputs.config_rope_tables(cf)
+        q0c, k0c, vc = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+        qc, kc = torch.empty_like(q0c), torch.empty_like(k0c)
+        w_q, w_k = torch.from_numpy(x["w_q"]).to(dev), torch.from_numpy(x["w_k"]).to(dev)
+        cos_d, sin_d = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+        wsc = torch.empty((attn_fwd_workspace_bytes(cf.B, cf.H, cf.Skv, cf.D),), dtype=torch.uint8, device=dev)
+        oc = torch.empty((cf.B, cf.H, cf.Sq, cf.D), dtype=torch.bfloat16, device=dev)
+        lc = torch.empty((cf.B, cf.H, cf.Sq), dtype=torch.float32, device=dev)
+
+        def step(e):
+            e[0].record()
+            qk_norm_rope_out(q0c, k0c, qc, kc, w_q, w_k, cos_d, sin_d, cf.eps)
+            e[1].record()
+            attn_fwd_ws(qc, kc, vc, wsc, out=oc, lse=lc, scale=cf.scale)
+            e[2].record()
+
+        t_pro, t_att = _time_calls(step, 3, reps, 2)
+        pro_bytes = 2 * (2 + 2) * cf.B * cf.H * cf.S * cf.D + 2 * cf.S * cf.D * 4
+        r = _attn_entry("attn_fwd_ws", t_att, cf.flops(),
+                        {"workload": f"{cf.name}: RMSNorm + RoPE prologue, attention over all keys",
+                         "prologue": _bw_entry(t_pro, pro_bytes)})
+        if not args.no_cpu_baseline:
+            rows = inputs.sample_rows(cf.index, cf.B, cf.H, cf.Sq, per_head=64)
+            ref_o, ref_l = oracle.attn(bits(qc), bits(kc), x["v"], cf.scale, False, rows=rows)
+            r["oracle_match"] = _match(oc, lc, rows, ref_o, ref_l, cf.D)
+        res[name] = r
+        del q0c, k0c, vc, qc, kc, wsc, oc, lc
+    return res
+
+
+def cpu_baseline(args, cfg, x, q, k, w_q, w_k, cos, sin, final_out, final_lse, ms_per_step) -> tuple:
+    """The oracle as it stands on this host's CPU share: attention on the
+    sampled rows (extrapolated linearly to every row, exact for non-causal
+    attention where each row costs 4*Skv*D FLOP), the prologue of q and k in
+    full (compared with the GPU prologue element by element) and an fp32
+    out/LSE merge of the step's full shape."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import compare
+    from attention_qk_norm_rope_amd import inputs
+    B, H, S, D = cfg.B, cfg.H, cfg.S, cfg.D
+    Sq, Skv = cfg.Sq, cfg.Skv
+    threads = oracle.default_threads()
+    rows = inputs.sample_rows(cfg.index, B, H, Sq, per_head=64)
+    log(f"[bench] cpu baseline: attention oracle on {rows.size} rows, {threads} threads")
+    q_bits = q.cpu().view(torch.int16).numpy().view(np.uint16)
+    k_bits = k.cpu().view(torch.int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    ref_o, ref_l = oracle.attn(q_bits, k_bits, x["v"], cfg.scale, False, rows=rows, nthreads=threads)
+    t_att = time.perf_counter() - t0
+    match = _match(final_out, final_lse, rows, ref_o, ref_l, D)
+    t_att_full = t_att * (B * H * Sq) / rows.size
+
+    # Prologue oracle over every row of q and k, one head at a time (bounded
+    # host memory), compared with the GPU prologue's output.
+    log("[bench] cpu baseline: prologue oracle over all of q and k")
+    t_pro = 0.0
+    worst = {"max_abs": 0.0, "n_above_atol": 0, "max_err_over_bound": 0.0}
+    dot = na = nb = 0.0
+    finite = True
+    for src, got, w in ((x["q"], q_bits, x["w_q"]), (x["k"], k_bits, x["w_k"])):
+        for b in range(B):
+            for h in range(H):
+                t0 = time.perf_counter()
+                ref = oracle.qk_norm_rope(np.ascontiguousarray(src[b:b + 1, h:h + 1]), w, cos, sin, cfg.eps,
+                                          nthreads=threads)
+                t_pro += time.perf_counter() - t0
+                g = inputs.bf16_bits_to_f64(got[b:b + 1, h:h + 1])
+                rep = compare.prologue_report(g, ref)
+                worst["max_abs"] = max(worst["max_abs"], rep["max_abs"])
+                worst["n_above_atol"] += rep["n_above_atol"]
+                worst["max_err_over_bound"] = max(worst["max_err_over_bound"], rep["max_err_over_bound"])
+                dot += float(np.dot(g.ravel(), ref.ravel()))
+                na += float(np.dot(g.ravel(), g.ravel()))
+                nb += float(np.dot(ref.ravel(), ref.ravel()))
+                finite = finite and bool(np.isfinite(g).all())
+    cos_sim = dot / math.sqrt(na * nb) if na > 0 and nb > 0 else 1.0
+    pro_match = {k2: round(v2, 8) if isinstance(v2, float) else v2 for k2, v2 in worst.items()}
+    pro_match["cos"] = round(cos_sim, 10)
+    pro_match["elements"] = int(2 * B * H * S * D)
+    pro_match["ok"] = bool(finite and worst["max_err_over_bound"] <= 1.0 and cos_sim >= compare.COS_MIN)
+
+    # Merge oracle over every row of the step's fp32 (out, lse) shape; the
+    # values are the step's output on both sides (the time does not depend
+    # on them).  It is timed in slices of heads.
+    log("[bench] cpu baseline: merge oracle over all rows")
+    t_mer = 0.0
+    for b in range(B):
+        for h0 in range(0, H, 8):
+            o = final_out[b, h0:h0 + 8].double().cpu().numpy()
+            l = final_lse[b, h0:h0 + 8].double().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.merge(o, l, o, l)
+            t_mer += time.perf_counter() - t0
+    total = t_att_full + t_pro + t_mer
+    base = {
+        "value": rows.size * 4.0 * Skv * D / t_att / 1e12, "unit": "TFLOP/s", "cores": threads,
+        "host_cpus": os.cpu_count(), "kind": "oracle",
+        "sample": (f"attention: {rows.size} query rows (64 per (b,h)) of the measured workload against all {Skv} "
+                   f"keys, fp64 two-pass softmax, {t_att:.1f} s, extrapolated to all {B * H * Sq} rows; "
+                   f"prologue: all of q and k in full, {t_pro:.1f} s; merge: all {B * H * Sq} rows in full "
+                   f"(single-threaded), {t_mer:.1f} s"),
+        "seconds": round(t_att, 2), "threads_note": "cores = the threads the oracle ran on: this process's CPU "
+                                                    "share (OMP_NUM_THREADS when set, else its CPU affinity)",
+        "attention_s_sampled": round(t_att, 2), "attention_s_extrapolated": round(t_att_full, 1),
+        "prologue_s_full": round(t_pro, 2), "merge_s_full": round(t_mer, 2),
+        "step_s_extrapolated": round(total, 1), "gpu_step_s": round(ms_per_step * 1e-3, 5),
+        "oracle_over_gpu": round(total / (ms_per_step * 1e-3), 0)}
+    return base, match, pro_match
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -249,7 +565,7 @@ def main():
     # One workspace, sized for the largest KV window of the step.
     ws_keys = {"wan": S - S // 4, "qwen": Skv, "cosmos": Skv, "sp": Skv // max(cfg.chunks, 1)}[wl]
     ws = torch.empty((attn_fwd_workspace_bytes(B, H, ws_keys, D),), dtype=torch.uint8, device=dev)
-
+    w_q = w_k = cos_d = sin_d = cos = sin = None
     if wl in ("wan", "qwen", "cosmos"):
         cos, sin = inputs.config_rope_tables(cfg)
         cos_d = torch.from_numpy(cos).to(dev)
@@ -282,14 +598,14 @@ def main():
     elif wl == "wan":
         c = S // 4
         out_a = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
-        out_b = torch.empty_like(out_a)
+        out_b = torch.empty_like(out_a) if not args.fuse_merge else None
         lse_a = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
         lse_b = torch.empty_like(lse_a)
         names = ["qk_norm_rope", "attn_fwd", "attn_fwd"] + ([] if args.fuse_merge else ["attn_merge"])
 
         def attn(q_, k_, v_, out, lse, merge):
-            # The query prologue either ran in place on q (q_ = q) or runs in
-            # the attention's Q load (q_ = q0, --fuse-q).
+            # The query prologue either ran on q (q_ = q) or runs in the
+            # attention's Q load (q_ = q0, --fuse-q).
             if merge:
                 attn_fwd_ws_merge(q_, k_, v_, ws, out, lse, scale=scale)
             elif args.fuse_q:
@@ -374,7 +690,9 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     evs = [mk() for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    clock = ClockSampler()
     torch.cuda.synchronize()
+    clock.start()
     t_wall = time.perf_counter()
     start.record()
     for i in range(args.steps):
@@ -382,20 +700,24 @@ def main():
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    sclk = clock.stop()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+    step_stats = _stats([ev[0].elapsed_time(ev[-1]) for ev in evs])
     log(f"[bench] {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
 
-    # Per-kernel durations (ms summed per step, averaged over steps).
+    # Per-kernel durations (ms summed per step).
     per_kernel = {}
     for ev in evs:
+        acc = {}
         for j, nm in enumerate(names):
-            per_kernel.setdefault(nm, []).append(ev[j].elapsed_time(ev[j + 1]))
+            acc[nm] = acc.get(nm, 0.0) + ev[j].elapsed_time(ev[j + 1])
+        for nm, t in acc.items():
+            per_kernel.setdefault(nm, []).append(t)
     launches = {nm: names.count(nm) for nm in set(names)}
 
     attn_flops = cfg.flops()
     if "attn_fwd" in per_kernel:
-        attn_ms_total = sum(per_kernel["attn_fwd"]) / args.steps          # per step
         n_attn = launches["attn_fwd"]
         entry = ("attn_fwd_ws (per call: v_prep_kernel, then attn_fwd_kernel; a last round that would fill at "
                  "most half the CUs runs as a second dispatch of 4-wave workgroups)")
@@ -403,29 +725,28 @@ def main():
             entry = ("attn_fwd_ws + attn_fwd_ws_merge (per call: v_prep_kernel, then attn_fwd_kernel; a last round "
                      "that would fill at most half the CUs runs as a second dispatch of 4-wave workgroups; the "
                      "second call merges into the first's output in its epilogue)")
+        attn_list = per_kernel["attn_fwd"]
     else:
         # Two streams: the interval spans both overlapped calls and the merge.
-        attn_ms_total = sum(per_kernel["attn_fwd+attn_merge"]) / args.steps
         n_attn = 2
         entry = ("attn_fwd_ring_overlap: 2 attn_fwd_ws calls on two streams + attn_merge "
                  "(avg_ms = overlapped span / 2)")
-    attn_launch_ms = attn_ms_total / n_attn
-    attn_tflops = attn_flops / (attn_ms_total * 1e-3) / 1e12
-    kernels["attn_fwd"] = {"entry": entry,
-                           "launches_per_step": n_attn, "avg_ms": round(attn_launch_ms, 4),
+        attn_list = per_kernel["attn_fwd+attn_merge"]
+    ast = _stats(attn_list)
+    attn_tflops = attn_flops / (ast["mean"] * 1e-3) / 1e12
+    kernels["attn_fwd"] = {"entry": entry, "launches_per_step": n_attn,
+                           "avg_ms": round(ast["mean"] / n_attn, 4),
+                           "median_ms": round(ast["median"] / n_attn, 4), "min_ms": round(ast["min"] / n_attn, 4),
                            "flop_per_step": attn_flops, "tflops": round(attn_tflops, 2),
+                           "tflops_median": round(attn_flops / (ast["median"] * 1e-3) / 1e12, 2),
+                           "tflops_best": round(attn_flops / (ast["min"] * 1e-3) / 1e12, 2),
                            "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}
     if "qk_norm_rope" in per_kernel:
-        pro_ms = sum(per_kernel["qk_norm_rope"]) / args.steps
         pro_bytes = (1 if args.fuse_q else 2) * (2 + 2) * B * H * S * D + 2 * S * D * 4
-        kernels["qk_norm_rope"] = {"avg_ms": round(pro_ms, 4), "bytes": pro_bytes,
-                                   "gbs": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
-                                   "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        kernels["qk_norm_rope"] = _bw_entry(per_kernel["qk_norm_rope"], pro_bytes)
     if n_merge:
-        mer_ms = sum(per_kernel["attn_merge"]) / args.steps / n_merge
-        kernels["attn_merge"] = {"launches_per_step": n_merge, "avg_ms": round(mer_ms, 4), "bytes": merge_bytes,
-                                 "gbs": round(merge_bytes / (mer_ms * 1e-3) / 1e9, 1),
-                                 "frac_hbm_peak": round(merge_bytes / (mer_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        kernels["attn_merge"] = _bw_entry([t / n_merge for t in per_kernel["attn_merge"]], merge_bytes)
+        kernels["attn_merge"]["launches_per_step"] = n_merge
 
     value = attn_flops / (ms_per_step * 1e-3) / 1e12
     flop_per_launch = attn_flops / n_attn
@@ -448,44 +769,54 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step_median": round(step_stats["median"], 3), "ms_per_step_min": round(step_stats["min"], 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 tensors; RMSNorm weights U(0.5,1.5))",
         "config": {"workload": workload_name, "B": B, "H": H, "Sq": Sq, "Skv": Skv, "D": D,
                    "causal": False, "scale": scale},
-        "roofline": roofline, "kernels": kernels,
+        "roofline": roofline, "kernels": kernels, "sclk": sclk,
     }
 
     if not args.no_cpu_baseline:
-        import oracle
-        from oracle import compare
-        rows = inputs.sample_rows(cfg.index, B, H, Sq, per_head=64)
-        log(f"[bench] cpu baseline: oracle on {rows.size} rows")
-        if wl == "sp":
-            q_bits, k_bits = x["q"], x["k"]
+        if wl == "sp" or args.fuse_q or args.ring_streams == 2 or wl != "wan":
+            # The per-workload runs keep the short baseline: attention rows only.
+            import oracle
+            rows = inputs.sample_rows(cfg.index, B, H, Sq, per_head=64)
+            log(f"[bench] cpu baseline: oracle on {rows.size} rows")
+            if wl == "sp":
+                q_bits, k_bits = x["q"], x["k"]
+            else:
+                if args.fuse_q:
+                    # The fused step never writes q: the attention saw the
+                    # prologue of q0, which qk_norm_rope reproduces bit for bit.
+                    q.copy_(q0)
+                    qk_norm_rope(q, None, w_q, None, cos_d, sin_d, cfg.eps)
+                    torch.cuda.synchronize()
+                q_bits = q.cpu().view(torch.int16).numpy().view(np.uint16)
+                k_bits = k.cpu().view(torch.int16).numpy().view(np.uint16)
+            threads = oracle.default_threads()
+            t0 = time.perf_counter()
+            ref_o, ref_l = oracle.attn(q_bits, k_bits, x["v"], scale, False, rows=rows, nthreads=threads)
+            t_cpu = time.perf_counter() - t0
+            result["cpu_baseline"] = {
+                "value": rows.size * 4.0 * Skv * D / t_cpu / 1e12, "unit": "TFLOP/s", "cores": threads,
+                "host_cpus": os.cpu_count(), "kind": "oracle",
+                "sample": f"{rows.size} query rows (64 per (b,h)) of the measured workload against all "
+                          f"{Skv} keys, fp64 two-pass softmax, {t_cpu:.1f} s",
+                "seconds": round(t_cpu, 2)}
+            result["oracle_match"] = _match(final_out, final_lse, rows, ref_o, ref_l, D)
         else:
-            if args.fuse_q:
-                # The fused step never writes q: the attention saw the prologue
-                # of q0, which qk_norm_rope reproduces bit for bit.
-                q.copy_(q0)
-                qk_norm_rope(q, None, w_q, None, cos_d, sin_d, cfg.eps)
-                torch.cuda.synchronize()
-            q_bits = q.cpu().view(torch.int16).numpy().view(np.uint16)
-            k_bits = k.cpu().view(torch.int16).numpy().view(np.uint16)
-        threads = oracle.default_threads()
-        t0 = time.perf_counter()
-        ref_o, ref_l = oracle.attn(q_bits, k_bits, x["v"], scale, False, rows=rows, nthreads=threads)
-        t_cpu = time.perf_counter() - t0
-        cpu_tflops = rows.size * 4.0 * Skv * D / t_cpu / 1e12
-        idx = torch.from_numpy(rows).to(dev)
-        got_o = final_out.reshape(-1, D).index_select(0, idx).double().cpu().numpy()
-        got_l = final_lse.reshape(-1).index_select(0, idx).double().cpu().numpy()
-        rep = compare.attn_report(got_o, ref_o, got_l, ref_l, bf16=final_out.dtype == torch.bfloat16)
-        result["cpu_baseline"] = {
-            "value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows.size} query rows (64 per (b,h)) of the measured workload against all "
-                      f"{Skv} keys, fp64 two-pass softmax, {t_cpu:.1f} s; prologue and merge not timed",
-            "seconds": round(t_cpu, 2)}
-        result["oracle_match"] = {k2: (round(v2, 8) if isinstance(v2, float) else v2) for k2, v2 in rep.items()}
+            base, match, pro_match = cpu_baseline(args, cfg, x, q, k, w_q, w_k, cos, sin, final_out, final_lse,
+                                                  ms_per_step)
+            result["cpu_baseline"] = base
+            result["oracle_match"] = match
+            result["prologue_oracle_match"] = pro_match
+
+    if wl == "wan" and not args.no_configs and args.ring_streams == 1 and not args.fuse_q:
+        wan = {"cfg": cfg, "q": q, "k": k, "v": v, "ws": ws, "q0": q0, "k0": k0, "to_dev": to_dev,
+               "v_bits": x["v"], "q0_bits": x["q"], "k0_bits": x["k"]}
+        del x
+        result["configs"] = run_configs(args, dev, wan)
     print(json.dumps(result), flush=True)
 
 

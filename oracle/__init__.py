@@ -67,12 +67,17 @@ def _load():
 
 
 def default_threads() -> int:
-    """Host threads for the oracle: the CPUs this process may use, at most 16."""
+    """Host threads for the oracle: every CPU this process may run on, or the
+    CPU share that OMP_NUM_THREADS states when it is set (a host with several
+    GPUs gives each GPU's jobs a share of its cores)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
 
 
 def _ptr(a: np.ndarray):

@@ -50,3 +50,22 @@ def workload(name: str) -> dict:
     """Host inputs of a config (cached for the session)."""
     say(f"[inputs] generating workload {name}")
     return inputs.make_inputs(inputs.WORKLOADS[name])
+
+
+def launch_edge_rows(B: int, H: int, Sq: int, cus: int = 256) -> list:
+    """Flat query rows at the edges of the workspace path's launch forms: the
+    first row of the first tile that the grid's mostly empty last round hands
+    to a second dispatch of 4-wave workgroups (and the first row of that
+    tile's second half), plus the rows either side of those edges."""
+    bm = 256
+    nq = (Sq + bm - 1) // bm
+    blk = nq * B * H
+    tail = blk % cus
+    rows = []
+    if 0 < tail <= cus // 2:
+        t = blk - tail
+        bh, qt = divmod(t, nq)
+        for r in (qt * bm - 1, qt * bm, qt * bm + bm // 2 - 1, qt * bm + bm // 2):
+            if 0 <= r < Sq:
+                rows.append(bh * Sq + r)
+    return rows

@@ -14,8 +14,8 @@ import torch
 import oracle
 from oracle import compare
 from attention_qk_norm_rope_amd import (attn_fwd, attn_fwd_ring_overlap, attn_fwd_workspace_bytes, attn_fwd_ws,
-                                        attn_merge, inputs, qk_norm_rope)
-from gpu_common import dev_bits, dev_f32, host_bits, host_f64, rows_of, say, workload
+                                        attn_fwd_ws_merge, attn_merge, inputs, qk_norm_rope, qk_norm_rope_out)
+from gpu_common import dev_bits, dev_f32, host_bits, host_f64, launch_edge_rows, rows_of, say, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -42,8 +42,8 @@ def _check_prologue_heads(cfg, x, dq, dk, cos, sin, heads=None):
         compare.assert_ok(rep, f"{cfg.name} prologue {name}")
 
 
-def _check_attn(cfg, q_bits, k_bits, v_bits, out, lse, tag):
-    rows = inputs.sample_rows(cfg.index, cfg.B, cfg.H, q_bits.shape[2])
+def _check_attn(cfg, q_bits, k_bits, v_bits, out, lse, tag, extra=()):
+    rows = inputs.sample_rows(cfg.index, cfg.B, cfg.H, q_bits.shape[2], extra=extra)
     say(f"[{cfg.name}] oracle on {rows.size} rows ({tag})")
     ref_o, ref_l = oracle.attn(q_bits, k_bits, v_bits, cfg.scale, False, rows=rows)
     rep = compare.attn_report(rows_of(out, rows), ref_o, rows_of(lse, rows), ref_l,
@@ -74,6 +74,43 @@ def test_wan_attention(times_four):
     out, lse = attn_fwd(dev_bits(qb), dev_bits(x["k"]), dev_bits(x["v"]), scale=cfg.scale)
     torch.cuda.synchronize()
     _check_attn(cfg, qb, x["k"], x["v"], out, lse, "q x4" if times_four else "plain")
+
+
+@pytest.mark.parametrize("times_four", [False, True], ids=["plain", "q_x4"])
+def test_wan_measured_step(times_four):
+    """The benchmark's default step at full size, call for call: the
+    out-of-place prologue of q and k, attn_fwd_ws over the local quarter of
+    the keys into fp32 (out, lse), then attn_fwd_ws_merge over the other
+    three quarters, merged into that output in the attention epilogue (one
+    workspace for both calls).  The Q x4 variant multiplies the normalised q
+    by 4 (exact in bf16) so that the logit std is about 4.  Sampled rows
+    include the 32-/128-/256-row block edges and the edges of the last-round
+    dispatch; the oracle consumes the GPU prologue's output."""
+    cfg = inputs.WORKLOADS["wan"]
+    x = workload("wan")
+    B, H, S, D = cfg.B, cfg.H, cfg.S, cfg.D
+    cos, sin = inputs.config_rope_tables(cfg)
+    q0, k0, v = dev_bits(x["q"]), dev_bits(x["k"]), dev_bits(x["v"])
+    q, k = torch.empty_like(q0), torch.empty_like(k0)
+    say(f"[wan] measured step ({'q x4' if times_four else 'plain'}): prologue")
+    qk_norm_rope_out(q0, k0, q, k, dev_f32(x["w_q"]), dev_f32(x["w_k"]), dev_f32(cos), dev_f32(sin), cfg.eps)
+    torch.cuda.synchronize()
+    del q0, k0
+    if times_four:
+        q.mul_(4)
+    c = S // 4
+    ws = torch.empty((attn_fwd_workspace_bytes(B, H, S - c, D),), dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, H, S, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    say("[wan] measured step: attn_fwd_ws (local quarter), attn_fwd_ws_merge (remote three quarters)")
+    attn_fwd_ws(q, k[:, :, :c], v[:, :, :c], ws, out=out, lse=lse, scale=cfg.scale)
+    attn_fwd_ws_merge(q, k[:, :, c:], v[:, :, c:], ws, out, lse, scale=cfg.scale)
+    torch.cuda.synchronize()
+    del ws
+    if not times_four:
+        _check_prologue_heads(cfg, x, q, k, cos, sin, heads=[0, 39])
+    _check_attn(cfg, host_bits(q), host_bits(k), x["v"], out, lse, "measured step" + (" q x4" if times_four else ""),
+                extra=launch_edge_rows(B, H, S))
 
 
 def test_wan_ring_overlap_step():
