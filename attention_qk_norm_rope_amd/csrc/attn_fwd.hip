@@ -40,10 +40,14 @@
 //    peaked softmax rows (a few dominant keys) bf16 P puts errors of ~1e-3
 //    into O; fp16 P makes them 8x smaller.
 //  * O^T lives in registers with one query per lane, so the online-softmax
-//    rescale multiplies by a per-lane scalar.  The running max only moves
-//    when a tile max exceeds it by more than TAU (log2 units); otherwise P is
-//    computed against the stale max (values <= 2^TAU, exact after the final
-//    division), and most tiles skip the O rescale.  O and the LSE use the sum
+//    rescale multiplies by a per-lane scalar.  P is first taken against the
+//    running max (a stale max is fine: any max gives the same result after
+//    the final division, as long as P stays in fp16 range and precision).
+//    When every lane of the wave has a tile sum below 2^TAU (so each of its
+//    P is at most 2^TAU, log2 units) that P stands and the tile max is not
+//    even computed; this is the common case once a row's max is known, and
+//    such tiles skip the O rescale.  Otherwise the running max moves up to
+//    the tile max wherever that is larger and P is taken again.  O and the LSE use the sum
 //    of the fp16-rounded P that multiplied V: the applied weights sum to 1,
 //    and the sum is within 2^-11 relative of the exact one.
 //  * exp is exp2 of fma(s, scale*log2(e), -m); the scale sign is folded into
@@ -86,8 +90,14 @@ constexpr int QPW = 32;                // query rows per wave
 constexpr int WAVES = 8;               // waves per workgroup (4 for small grids, workspace path)
 constexpr int SMALL_GRID_ROUNDS = 24;  // causal grids: 4-wave workgroups only below this many 8-wave rounds
 constexpr float LN2 = 0.69314718055994531f;
-constexpr float TAU = 8.0f;            // lazy-rescale threshold, log2 units
+constexpr float TAU = 8.0f;            // P <= 2^TAU (log2 units) keeps fp16 P in range and precision
+constexpr float P_SUM_FAST = 256.0f;   // 2^TAU: a lane's tile sum below it bounds each of its P
 constexpr int RSRC_WORD3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
+#ifndef DIT_PP_OFFSET
+#define DIT_PP_OFFSET 1
+#endif
+constexpr bool PP_OFFSET = DIT_PP_OFFSET;  // the two wave groups run one phase apart
+constexpr bool PP_PRIO = true;         // ping-pong form: raise the wave priority during MFMA phases
 
 // A wave-uniform value moved to a scalar register.
 __device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -161,9 +171,10 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[KB], int kv0, int Skv, boo
         }
 }
 
-// Row max of a tile's scores (both lane halves) and the lazy-rescale update.
+// Row max of a tile's scores (both lane halves) and the running-max update:
+// the max moves when the tile max exceeds it by more than tau.
 template <int KB>
-__device__ __forceinline__ void tile_max(const f32x16 (&s)[KB], float c, float& m_run, float& alpha,
+__device__ __forceinline__ void tile_max(const f32x16 (&s)[KB], float c, float tau, float& m_run, float& alpha,
                                          bool& grow) {
     float mx = s[0][0];
 #pragma unroll
@@ -172,7 +183,7 @@ __device__ __forceinline__ void tile_max(const f32x16 (&s)[KB], float c, float& 
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = pair_max(mx);
     const float m_new = mx * c;
-    grow = m_new > m_run + TAU;
+    grow = m_new > m_run + tau;
     alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = grow ? m_new : m_run;
 }
@@ -239,6 +250,79 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run
     if (lse && hh == 0) lse[lrow] = lm;
 }
 
+// Q fragments of query row qi (lane half hh): qf[t] holds elements
+// 16t + 8hh .. +7 of the row, the B operand of the score MFMA of k-step t.
+// FQ: the row is raw and gets the RMSNorm + rotary of qk_norm_rope on the way
+// (same bits): the lane holds the 16-byte chunks ch = 2t + hh of its row, so
+// the xor tree of chunk sums (partners D/16 chunks apart first) is a tree
+// over t followed by the cross-half pair.  The scale's sign goes into Q.
+template <int D, bool FQ>
+__device__ __forceinline__ void load_q(const uint16_t* qbh, int Sq, int qi, int hh, unsigned qsign,
+                                       const QNormRope& qn, bf16x8 (&qf)[D / 16]) {
+    constexpr int DT = D / 16;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qbh, (short)0, Sq * D * 2,
+                                                                        RSRC_WORD3);
+    if constexpr (!FQ) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * D + 16 * t + 8 * hh) * 2, 0, 0);
+            x ^= qsign;
+            qf[t] = __builtin_bit_cast(bf16x8, x);
+        }
+    } else {
+        unsigned raw[DT][4];
+        float cs[DT];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * D + 16 * t + 8 * hh) * 2, 0, 0);
+            float xv[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) raw[t][i] = x[i];
+            nr::unpack8(raw[t], xv);
+            cs[t] = nr::chunk_sumsq(xv);
+        }
+#pragma unroll
+        for (int m = DT / 2; m >= 1; m >>= 1)
+#pragma unroll
+            for (int t = 0; t < m; ++t) cs[t] += cs[t + m];
+        const float total = pair_sum(cs[0]);
+        const float inv_r = qi < Sq ? nr::rms_inv(total, 1.0f / (float)D, qn.eps) : 0.f;
+        // Tables [Sq, D]: rows past Sq read as zeros.
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void*)qn.cos_t, (short)0, Sq * D * 4,
+                                                                            RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)qn.sin_t, (short)0, Sq * D * 4,
+                                                                            RSRC_WORD3);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const int d0 = 16 * t + 8 * hh;
+            const f32x4 w0 = *(const f32x4*)(qn.w + d0), w1 = *(const f32x4*)(qn.w + d0 + 4);
+            // Whole-vector bit casts: a bit cast of one element of a vector
+            // (an lvalue) is lowered as element 0 by this compiler.
+            const f32x4 c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (qi * D + d0) * 4, 0, 0));
+            const f32x4 c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (qi * D + d0 + 4) * 4, 0, 0));
+            const f32x4 s0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (qi * D + d0) * 4, 0, 0));
+            const f32x4 s1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (qi * D + d0 + 4) * 4, 0, 0));
+            const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+            float cv[8], sv[8], xv[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cv[i] = c0[i];
+                cv[i + 4] = c1[i];
+                sv[i] = s0[i];
+                sv[i + 4] = s1[i];
+            }
+            nr::unpack8(raw[t], xv);
+            u32x4 r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                r[i] = nr::pair(xv[2 * i], xv[2 * i + 1], inv_r, wv[2 * i], wv[2 * i + 1], cv[2 * i], cv[2 * i + 1],
+                                sv[2 * i], sv[2 * i + 1]);
+            r ^= qsign;
+            qf[t] = __builtin_bit_cast(bf16x8, r);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Main loop: sub-iteration j issues three independent streams
 // of work so that one wave keeps both the MFMA pipe and the VALU busy: the
@@ -296,73 +380,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     const int q0w = q0 + wave * QPW;
     const int n_vt = (Skv_all + BN - 1) / BN;     // tiles of the V image
 
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(q + (int64_t)bh * Sq * D), (short)0, Sq * D * 2, RSRC_WORD3);
     bf16x8 qf[DT];
-    if constexpr (!FQ) {
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, ((q0w + n) * D + 16 * t + 8 * hh) * 2, 0, 0);
-            x ^= qsign;
-            qf[t] = __builtin_bit_cast(bf16x8, x);
-        }
-    } else {
-        // RMSNorm + rotary of the raw query row, as qk_norm_rope computes it:
-        // the lane holds the 16-byte chunks ch = 2t + hh of its row, so the
-        // xor tree of chunk sums (partners D/16 chunks apart first) is a tree
-        // over t followed by the cross-half pair.
-        const int qi = q0w + n;
-        unsigned raw[DT][4];
-        float cs[DT];
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, (qi * D + 16 * t + 8 * hh) * 2, 0, 0);
-            float xv[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) raw[t][i] = x[i];
-            nr::unpack8(raw[t], xv);
-            cs[t] = nr::chunk_sumsq(xv);
-        }
-#pragma unroll
-        for (int m = DT / 2; m >= 1; m >>= 1)
-#pragma unroll
-            for (int t = 0; t < m; ++t) cs[t] += cs[t + m];
-        const float total = pair_sum(cs[0]);
-        const float inv_r = qi < Sq ? nr::rms_inv(total, 1.0f / (float)D, qn.eps) : 0.f;
-        // Tables [Sq, D]: rows past Sq read as zeros.
-        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void*)qn.cos_t, (short)0, Sq * D * 4,
-                                                                            RSRC_WORD3);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)qn.sin_t, (short)0, Sq * D * 4,
-                                                                            RSRC_WORD3);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            const int d0 = 16 * t + 8 * hh;
-            const f32x4 w0 = *(const f32x4*)(qn.w + d0), w1 = *(const f32x4*)(qn.w + d0 + 4);
-            // Whole-vector bit casts: a bit cast of one element of a vector
-            // (an lvalue) is lowered as element 0 by this compiler.
-            const f32x4 c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (qi * D + d0) * 4, 0, 0));
-            const f32x4 c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (qi * D + d0 + 4) * 4, 0, 0));
-            const f32x4 s0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (qi * D + d0) * 4, 0, 0));
-            const f32x4 s1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (qi * D + d0 + 4) * 4, 0, 0));
-            const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-            float cv[8], sv[8], xv[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                cv[i] = c0[i];
-                cv[i + 4] = c1[i];
-                sv[i] = s0[i];
-                sv[i + 4] = s1[i];
-            }
-            nr::unpack8(raw[t], xv);
-            u32x4 r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                r[i] = nr::pair(xv[2 * i], xv[2 * i + 1], inv_r, wv[2 * i], wv[2 * i + 1], cv[2 * i], cv[2 * i + 1],
-                                sv[2 * i], sv[2 * i + 1]);
-            r ^= qsign;
-            qf[t] = __builtin_bit_cast(bf16x8, r);
-        }
-    }
+    load_q<D, FQ>(q + (int64_t)bh * Sq * D, Sq, q0w + n, hh, qsign, qn, qf);
 
     int n_tiles = (Skv + BN - 1) / BN;
     if (causal) {
@@ -495,7 +514,6 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[t & 1][i], pp[kb][u], o[db], 0, 0, 0);
             }
             if (t == 0) {
-                tile_max(sc, c, m_run, alpha, grow);
                 neg_m = -m_run;
             } else {
                 // 16 units (kb, u, e) of two scores each, spread over chunks 1..NCH-1.
@@ -512,6 +530,22 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
                 if (t == NCH / 2) load_v(kv0);
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // P was taken against the running max.  Unless every lane's tile sum
+        // is below 2^TAU (so each P is at most 2^TAU), the running max moves
+        // up to the tile max wherever that is larger, and P is taken again
+        // against the new max.
+        if (!__all(lsum < P_SUM_FAST)) {
+            tile_max(sc, c, 0.f, m_run, alpha, grow);
+            if (grow) {
+                lsum = 0.f;
+                neg_m = -m_run;
+#pragma unroll
+                for (int unit = 0; unit < 16; ++unit) {
+                    const int kb = unit / 8, u = (unit / 4) % 2, e = unit % 4;
+                    w4[kb][u][e] = p_pair(sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1], c, neg_m, lsum);
+                }
+            }
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -586,6 +620,289 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse);
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong form of the same computation (8-wave workgroups over the
+// workspace, full attention).  The waves form two groups of four, and each
+// SIMD runs one wave of each group.  A wave alternates two phases per 64-key
+// tile j:
+//   M(j): the 16 score MFMAs S_j = K_j Q^T and the 16 P V MFMAs
+//         O += V_{j-1}^T P_{j-1}^T, with the LDS fragment reads between them;
+//   V(j): the softmax of S_j (mask, tile max, lazy rescale, exp2, fp16 P, row
+//         sum) and the fragment reads that start M(j+1).
+// Group 1 runs one phase behind group 0, and every phase ends at a workgroup
+// barrier, so on each SIMD one wave feeds the MFMA pipe while the other keeps
+// the VALU busy; the roles swap at each barrier.  Per row, the operations and
+// their order are those of attn_fwd_kernel (same bits).
+// K and V tiles sit in three LDS buffers each (tile t in buffer t mod 3).
+// The DMAs of K_{j+2} and V_{j+1} are issued in the phase pair that starts
+// with group 0's M(j); each wave waits for its own part of them two phases
+// later (vmcnt), and they are read after the barrier that follows.
+template <int D, bool OUT_F32, bool FQ, bool MERGE>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+               const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
+               float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
+               int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
+               const int* __restrict__ lkv, int out_heads, int out_h0, int tile0, int halves) {
+    constexpr int W = 8;
+    constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
+    constexpr int TILE = BN * D;
+    constexpr int KDMA = TILE * 2 / 1024 / W;         // 1 KB DMA chunks per wave per tile
+    constexpr int NSTEP = KB * DT;                    // score MFMAs per tile = P V MFMAs per tile
+    static_assert(KDMA >= 1 && KDMA * W * 1024 == TILE * 2, "tile shape");
+    static_assert(NSTEP == KB * 2 * DB, "pairs of one score and one P V MFMA");
+    constexpr int PF = 2;                             // fragment prefetch distance (steps)
+    constexpr int NR = PF + 1;                        // fragment registers in the ring
+    // vmcnt that leaves one tile's DMAs (2*KDMA per wave) in flight.
+    constexpr int WAIT_ONE_BATCH = 0x0F70 | (2 * KDMA);
+
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks2[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt2[TILE];
+    auto Kbuf = [&](auto bc) -> uint16_t* {
+        constexpr int b = decltype(bc)::value % 3;
+        if constexpr (b == 0) return Ks0; else if constexpr (b == 1) return Ks1; else return Ks2;
+    };
+    auto Vbuf = [&](auto bc) -> uint16_t* {
+        constexpr int b = decltype(bc)::value % 3;
+        if constexpr (b == 0) return Vt0; else if constexpr (b == 1) return Vt1; else return Vt2;
+    };
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x) + tile0;
+    const int bh = logical / n_qtiles;
+    const int bkv = kv_head(bh, H, G);
+    const int Sq_b = lq ? min(max(lq[bh / H], 0), Sq) : Sq;
+    const int Skv = lkv ? min(max(lkv[bh / H], 0), Skv_all) : Skv_all;
+    const int q0 = (logical - bh * n_qtiles) * (W * QPW);
+
+    const int tid = threadIdx.x;
+    const int wave = uniform_int(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
+    const int grp = wave >> 2;
+    const int q0w = q0 + wave * QPW;
+    const int n_vt = (Skv_all + BN - 1) / BN;
+
+    bf16x8 qf[DT];
+    load_q<D, FQ>(q + (int64_t)bh * Sq * D, Sq, q0w + n, hh, qsign, qn, qf);
+
+    const int n_tiles = q0 >= Sq_b ? 0 : (Skv + BN - 1) / BN;
+
+    const uint16_t* kbh = k + (int64_t)bkv * kv_bh_stride;
+    auto dma_k = [&](int tile, auto b) {
+        const int kv0 = tile * BN;
+        const int left = Skv - kv0;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kbh + (int64_t)kv0 * D), (short)0, left > 0 ? left * D * 2 : 0, RSRC_WORD3);
+#pragma unroll
+        for (int i = 0; i < KDMA; ++i) {
+            const int s = (wave * KDMA + i) * 64 + lane;
+            const int key = s / SL;
+            const int slot = (s % SL) ^ kswz<D>(key);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Kbuf(b) + (wave * KDMA + i) * 512), 16,
+                                                     (key * D + 8 * slot) * 2, 0, 0, 0);
+        }
+    };
+    const uint16_t* vbh = vws + (int64_t)bkv * n_vt * TILE;
+    auto dma_v = [&](int tile, auto b) {
+        // Tiles past the image read as zeros.
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vbh + (int64_t)min(tile, n_vt - 1) * TILE), (short)0, tile < n_vt ? TILE * 2 : 0, RSRC_WORD3);
+#pragma unroll
+        for (int i = 0; i < KDMA; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Vbuf(b) + (wave * KDMA + i) * 512), 16,
+                                                     ((wave * KDMA + i) * 64 + lane) * 16, 0, 0, 0);
+    };
+    auto kfrag = [&](auto b, int kb, int t) {
+        const int key = 32 * kb + n;
+        const int slot = (2 * t + hh) ^ kswz<D>(key);
+        return __builtin_bit_cast(bf16x8, *(const u32x4*)(Kbuf(b) + key * D + 8 * slot));
+    };
+    auto vfrag = [&](auto b, int kb, int u, int db) {
+        const int row = 32 * db + n;
+        const int lslot = 4 * kb + 2 * u + hh;
+        return __builtin_bit_cast(f16x8, *(const u32x4*)(Vbuf(b) + row * BN + 8 * (lslot ^ ((row >> 1) & 7))));
+    };
+    // Step i of a phase M: score MFMA (kb = i % KB, k-step i / KB) and
+    // P V MFMA (index i = db + DB (u + 2 kb)).
+    auto pv_idx = [](int i, int& kb, int& u, int& db) {
+        kb = i / (2 * DB);
+        u = (i / DB) % 2;
+        db = i % DB;
+    };
+    auto barrier = []() { asm volatile("s_barrier" ::: "memory"); };
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 s[KB];
+    f16x8 p[KB][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) p[kb][u] = f16x8{};
+    bf16x8 kf[NR];
+    f16x8 vf[NR];
+
+    // Fragments of step i of phase M(j): K_j in buffer bj, V_{j-1} in bv.
+    auto load_step = [&](auto bj, auto bv, int i) {
+        int kb, u, db;
+        pv_idx(i, kb, u, db);
+        kf[i % NR] = kfrag(bj, i % KB, i / KB);
+        vf[i % NR] = vfrag(bv, kb, u, db);
+    };
+
+    // Prologue: K_0, K_1, V_0 by DMA; zeros in the buffer of V_{-1} (tile -1
+    // mod 3 = 2), which P_{-1} = 0 multiplies in M(0).
+    dma_k(0, B0{});
+    dma_k(1, B1{});
+    dma_v(0, B0{});
+#pragma unroll
+    for (int i = 0; i < TILE / (W * 512); ++i)
+        *(u32x4*)(Vt2 + (i * W * 64 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    barrier();
+
+    using B2 = std::integral_constant<int, 2>;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) load_step(B0{}, B2{}, i);
+
+    // One tile: M(j) then V(j) of group GRP.  b = j mod 3 selects the buffers.
+    // Each group runs its own copy of the loop, so the DMAs sit at fixed
+    // points of each copy (the compiler then sees which are in flight).
+    auto tile_step = [&](auto gc, auto bc, int j) __attribute__((always_inline)) {
+        constexpr int GRP = decltype(gc)::value;
+        constexpr int b = decltype(bc)::value;
+        using BK = std::integral_constant<int, b>;             // K_j
+        using BV = std::integral_constant<int, (b + 2) % 3>;   // V_{j-1}
+        using BN1 = std::integral_constant<int, (b + 1) % 3>;  // K_{j+1}, V_{j+1}
+        using BN2 = std::integral_constant<int, (b + 2) % 3>;  // K_{j+2}
+        // ---- M(j)
+        if constexpr (GRP == 0 || GRP == 2) {
+            dma_k(j + 2, BN2{});
+            dma_v(j + 1, BN1{});
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+        if constexpr (PP_PRIO) __builtin_amdgcn_s_setprio(1);
+        // Step i: the fragment reads of step i + PF, then the two MFMAs of
+        // step i (fenced, so the reads stay PF steps ahead).
+#pragma unroll
+        for (int i = 0; i < NSTEP; ++i) {
+            if (i + PF < NSTEP) load_step(BK{}, BV{}, i + PF);
+            int kb, u, db;
+            pv_idx(i, kb, u, db);
+            s[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % NR], qf[i / KB], s[i % KB], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % NR], p[kb][u], o[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (PP_PRIO) __builtin_amdgcn_s_setprio(0);
+        // Group 0: its DMAs of the phase pair before have landed (one batch,
+        // issued at the start of this phase, stays in flight).
+        if constexpr (GRP == 0) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);
+        if constexpr (GRP != 2) barrier();
+        // ---- V(j)
+        if constexpr (GRP == 1) {
+            dma_k(j + 3, BK{});
+            dma_v(j + 2, BN2{});
+        }
+        const int kv0 = j * BN;
+        if (kv0 + BN > Skv) mask_tile(s, kv0, Skv, false, 0, hh);
+        // Softmax of the tile (the same rule as attn_fwd_kernel, see there).
+        float alpha = 1.0f, lsum = 0.f;
+        bool grow = false;
+        u32x4 w4[KB][2];
+        auto make_p = [&](float neg_m) __attribute__((always_inline)) {
+            lsum = 0.f;
+#pragma unroll
+            for (int unit = 0; unit < 16; ++unit) {
+                const int kb = unit / 8, u = (unit / 4) % 2, e = unit % 4;
+                w4[kb][u][e] = p_pair(s[kb][8 * u + 2 * e], s[kb][8 * u + 2 * e + 1], c, neg_m, lsum);
+            }
+        };
+        make_p(-m_run);
+        if (!__all(lsum < P_SUM_FAST)) {
+            tile_max(s, c, 0.f, m_run, alpha, grow);
+            if (grow) make_p(-m_run);
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) p[kb][u] = __builtin_bit_cast(f16x8, w4[kb][u]);
+        l_run = __builtin_fmaf(l_run, alpha, lsum);
+        if (__any(grow && l_run >= 0.f)) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+        // First fragments of M(j+1): K_{j+1}, and V_j (buffer b).
+#pragma unroll
+        for (int i = 0; i < PF; ++i) load_step(BN1{}, BK{}, i);
+        if constexpr (GRP == 1) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);   // its DMAs of the pair before
+        if constexpr (GRP == 2) __builtin_amdgcn_s_waitcnt(0x0F70);           // this tile's DMAs have landed
+        barrier();
+    };
+
+    // Last P V: O += V_{n-1}^T P_{n-1}^T, V_{n-1} in buffer (n-1) mod 3; its
+    // first fragments were loaded at the end of V(n-1) (with the unused K
+    // fragments of a tile past the end).
+    auto last_pv = [&](auto bv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NSTEP; ++i) {
+            int kb, u, db;
+            pv_idx(i, kb, u, db);
+            const f16x8 vv = i < PF ? vf[i % NR] : vfrag(bv, kb, u, db);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, p[kb][u], o[db], 0, 0, 0);
+        }
+    };
+
+    auto run = [&](auto gc) __attribute__((always_inline)) {
+        constexpr int GRP = decltype(gc)::value;
+        if constexpr (GRP == 1) {
+            // Group 1 idles for the first phase; it issues its part of the
+            // DMAs of the first phase pair (K_2, V_1) there.
+            dma_k(2, B2{});
+            dma_v(1, B1{});
+            barrier();
+        }
+        int j = 0;
+        for (; j + 3 <= n_tiles; j += 3) {
+            tile_step(gc, B0{}, j);
+            tile_step(gc, B1{}, j + 1);
+            tile_step(gc, B2{}, j + 2);
+        }
+        if (j < n_tiles) {
+            tile_step(gc, B0{}, j);
+            if (++j < n_tiles) tile_step(gc, B1{}, j);
+        }
+        // Group 1 is one phase behind: its last barrier ended V(n-1); group 0
+        // takes the matching barrier after its last P V.  The DMAs of tiles
+        // past the end (zeros) are drained before the workgroup can end.
+        const int lb = (n_tiles + 2) % 3;       // buffer of tile n-1 (tile -1 when n = 0)
+        if (lb == 0) last_pv(B0{});
+        else if (lb == 1) last_pv(B1{});
+        else last_pv(B2{});
+        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
+        if constexpr (GRP == 0) barrier();
+    };
+    if constexpr (!PP_OFFSET) run(std::integral_constant<int, 2>{});
+    else if (grp == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+
+    const int qi = q0w + n;
+    const int64_t lrow = (int64_t)bh * Sq + qi;
+    const int64_t orow = out_heads ? ((int64_t)(bh / H) * Sq + qi) * out_heads + out_h0 + bh % H : lrow;
+    store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse);
+}
+
 template <int D, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
                   int BH, int H, int G, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
@@ -618,20 +935,25 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
     // is small.
     const bool tail_split = vws != nullptr && !causal && tail8 > 0 && tail8 <= 128;
     const bool all4 = vws != nullptr && causal && blk8 < (int64_t)SMALL_GRID_ROUNDS * 256 && tail8 > 0 && tail8 <= 128;
-    auto run = [&](auto k8, auto k4, const QNormRope& qa) -> hipError_t {
+    // Full attention over the workspace runs its 8-wave workgroups in the
+    // ping-pong form (same bits).
+    auto run = [&](auto k8, auto k4, auto kpp, const QNormRope& qa) -> hipError_t {
         if (all4) return go(k4, qa, 4, (Sq + 4 * QPW - 1) / (4 * QPW), 0, (int64_t)((Sq + 4 * QPW - 1) / (4 * QPW)) * BH,
                             false);
-        if (!tail_split) return go(k8, qa, WAVES, nq8, 0, blk8, false);
-        const hipError_t e = go(k8, qa, WAVES, nq8, 0, full8, false);
+        if (!tail_split) return causal ? go(k8, qa, WAVES, nq8, 0, blk8, false) : go(kpp, qa, WAVES, nq8, 0, blk8, false);
+        const hipError_t e = go(kpp, qa, WAVES, nq8, 0, full8, false);
         if (e != hipSuccess) return e;
         return go(k4, qa, 4, nq8, full8, tail8, true);
     };
     if (merge)
-        return run(attn_fwd_kernel<D, OUT_F32, false, true, true>, attn_fwd_kernel<D, OUT_F32, false, true, true, 4>, qz);
+        return run(attn_fwd_kernel<D, OUT_F32, false, true, true>, attn_fwd_kernel<D, OUT_F32, false, true, true, 4>,
+                   attn_pp_kernel<D, OUT_F32, false, true>, qz);
     if (vws && qn)
-        return run(attn_fwd_kernel<D, OUT_F32, true, true>, attn_fwd_kernel<D, OUT_F32, true, true, false, 4>, *qn);
+        return run(attn_fwd_kernel<D, OUT_F32, true, true>, attn_fwd_kernel<D, OUT_F32, true, true, false, 4>,
+                   attn_pp_kernel<D, OUT_F32, true, false>, *qn);
     if (vws)
-        return run(attn_fwd_kernel<D, OUT_F32, false, true>, attn_fwd_kernel<D, OUT_F32, false, true, false, 4>, qz);
+        return run(attn_fwd_kernel<D, OUT_F32, false, true>, attn_fwd_kernel<D, OUT_F32, false, true, false, 4>,
+                   attn_pp_kernel<D, OUT_F32, false, false>, qz);
     return go(attn_fwd_kernel<D, OUT_F32, false, false>, qz, WAVES, nq8, 0, blk8, false);
 }
 
