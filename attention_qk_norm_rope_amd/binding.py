@@ -55,11 +55,13 @@ def _load():
     lib.attn_fwd_ws_bsnd.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, p]
     lib.attn_fwd_ws_merge.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_merge.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p]
+    lib.attn_fwd_noalloc.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_varlen.argtypes = [p, p, p, p, i64, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     for name in ("qk_norm_rope", "qk_norm_rope_out", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_fwd_ws_fused_q",
-                 "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd"):
+                 "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd",
+                 "attn_fwd_noalloc"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -275,6 +277,20 @@ def attn_fwd_ws(q, k, v, workspace, out=None, lse=None, scale: float | None = No
                              _ptr(lse), B, H, Sq, Skv, D, scale, 1 if causal else 0, _dtype_code(out),
                              _stream())
     _check("attn_fwd_ws", st)
+    return out, lse
+
+
+def attn_fwd_noalloc(q, k, v, out=None, lse=None, scale: float | None = None, causal: bool = False,
+                     out_dtype=torch.bfloat16, return_lse: bool = True):
+    """attn_fwd_ws with the library's static scratch buffer in place of a
+    workspace: the library call allocates no device memory (pass out and lse
+    to allocate nothing here either).  Same bits as attn_fwd_ws.  Calls that
+    may overlap on one GPU share that buffer and must be ordered on one
+    stream."""
+    (B, H, Sq, Skv, D), sk, scale, out, lse = _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse)
+    st = _load().attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), sk, _ptr(out), _ptr(lse), B, H, Sq, Skv, D, scale,
+                                  1 if causal else 0, _dtype_code(out), _stream())
+    _check("attn_fwd_noalloc", st)
     return out, lse
 
 

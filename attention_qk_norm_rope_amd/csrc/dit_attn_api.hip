@@ -8,6 +8,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace {
 
 struct Range {
@@ -323,6 +325,80 @@ int bnsd_to_bsnd(const void* o, void* x, int B, int S, int H, int h0, int Hs, in
     return hip_status(dit::launch_layout(o, x, B, S, H, h0, Hs, D, false, stream));
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// attn_fwd_noalloc: attn_fwd_ws with its V-image workspace in a static device
+// array instead of a caller buffer.  The array lives in this file; host code
+// reaches it only through the address hipGetSymbolAddress returns for the
+// current device (its name is a host-side stand-in, not a device address).
+
+namespace {
+
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;   // DIT_NOALLOC_SCRATCH_BYTES
+static_assert(kScratchBytes == DIT_NOALLOC_SCRATCH_BYTES, "header and library agree on the scratch size");
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) static unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on each device, looked up on the first call
+// there (with that device current) and kept until the process ends.
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+int scratch_address(hipStream_t stream, void** addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DIT_ERR_HIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return DIT_ERR_HIP;
+        if ((int)sdev != dev) return DIT_ERR_DEVICE;
+    }
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DIT_ERR_HIP;
+        g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    *addr = p;
+    return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
+                     int B, int H, int Sq, int Skv, int D, float scale, int causal, int out_dtype,
+                     hipStream_t stream) {
+    AttnRanges r;
+    const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, H, Sq, Skv, D, scale, out_dtype, &r);
+    if (st != DIT_OK) return st;
+    // Heads whose V images fit in the scratch together run as one group;
+    // the groups run one after another on the stream.
+    const int64_t per_head = dit::v_prep_bytes(1, Skv, D);
+    if (per_head > kScratchBytes) return DIT_ERR_SCRATCH;
+    const int64_t BH = (int64_t)B * H;
+    const int64_t group = BH < kScratchBytes / per_head ? BH : kScratchBytes / per_head;
+    void* ws = nullptr;
+    const int sa = scratch_address(stream, &ws);
+    if (sa != DIT_OK) return sa;
+    const int64_t esize = out_dtype == DIT_FP32 ? 4 : 2;
+    (void)hipGetLastError();
+    for (int64_t h0 = 0; h0 < BH; h0 += group) {
+        const int n = (int)(BH - h0 < group ? BH - h0 : group);
+        const char* qg = (const char*)q + h0 * Sq * D * 2;
+        const char* kg = (const char*)k + h0 * kv_bh_stride * 2;
+        const char* vg = (const char*)v + h0 * kv_bh_stride * 2;
+        char* og = (char*)out + h0 * Sq * D * esize;
+        float* lg = lse ? lse + h0 * Sq : nullptr;
+        hipError_t e = dit::launch_v_prep(vg, kv_bh_stride, ws, n, Skv, D, nullptr, n, stream);
+        if (e != hipSuccess) return DIT_ERR_HIP;
+        e = dit::launch_attn_fwd(qg, kg, vg, kv_bh_stride, og, lg, n, n, 1, Sq, Skv, D, scale, causal != 0,
+                                 out_dtype == DIT_FP32, ws, nullptr, nullptr, nullptr, 0, 0, false, stream);
+        if (e != hipSuccess) return DIT_ERR_HIP;
+    }
+    return DIT_OK;
+}
+
 const char* dit_attn_status_string(int status) {
     switch (status) {
         case DIT_OK: return "ok";
@@ -332,6 +408,8 @@ const char* dit_attn_status_string(int status) {
         case DIT_ERR_ALIGN: return "pointer or stride breaks the alignment rule";
         case DIT_ERR_ALIAS: return "an output overlaps an input it must not overlap";
         case DIT_ERR_HIP: return "the HIP runtime reported a launch error";
+        case DIT_ERR_SCRATCH: return "one head's V images exceed the library's static scratch buffer";
+        case DIT_ERR_DEVICE: return "the stream belongs to another device than the current one";
         default: return "unknown status";
     }
 }

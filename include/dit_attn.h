@@ -10,6 +10,7 @@
  *   attn_fwd_ws_fused_q  attention with the query prologue fused into its Q load
  *   attn_fwd_ws_bsnd  attention storing its output into a head slice of a BSND tensor
  *   attn_fwd_ws_merge  attention over one key chunk merged into a running (out, lse)
+ *   attn_fwd_noalloc  attn_fwd_ws with its workspace in a static device buffer
  *   attn_merge     fold of two partial attentions over disjoint key sets
  *   bsnd_to_bnsd, bnsd_to_bsnd  head-slice layout change of Ulysses sequence parallelism
  *
@@ -32,8 +33,10 @@
  *   - D must be 64 or 128.  All sizes must be >= 1.  Offsets are 64-bit.
  *   - Tensor pointers must be 16-byte aligned; lse pointers 4-byte aligned.
  *   - The caller owns every buffer.  The library allocates nothing, frees
- *     nothing, never synchronises, prints nothing and keeps no mutable
- *     global state; calls are thread-safe and reentrant.
+ *     nothing, never synchronises and prints nothing.  Its only mutable
+ *     global state is the static scratch buffer of attn_fwd_noalloc (and the
+ *     per-device address of it); every other call is thread-safe and
+ *     reentrant.
  *   - Each call validates its arguments, then only enqueues work on
  *     `stream` (NULL = the default stream) and returns.  Buffers must stay
  *     alive until that work completes.  Invalid arguments are reported
@@ -59,7 +62,9 @@ enum dit_attn_status {
     DIT_ERR_UNSUPPORTED = 3, /* D not in {64,128}, or an unknown dtype code */
     DIT_ERR_ALIGN = 4,       /* a pointer or stride breaks the alignment rule */
     DIT_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
-    DIT_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+    DIT_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+    DIT_ERR_SCRATCH = 7,     /* attn_fwd_noalloc: the shape needs more than its static scratch */
+    DIT_ERR_DEVICE = 8       /* attn_fwd_noalloc: the stream is not on the current device */
 };
 
 enum dit_attn_dtype {
@@ -317,6 +322,31 @@ int bsnd_to_bnsd(const void *x, void *out, int B, int S, int H, int h0, int Hs, 
                  hipStream_t stream);
 int bnsd_to_bsnd(const void *o, void *x, int B, int S, int H, int h0, int Hs, int D,
                  hipStream_t stream);
+
+/*
+ * attn_fwd_ws without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the V images that attn_fwd_ws writes into its
+ * workspace go to a static device buffer of DIT_NOALLOC_SCRATCH_BYTES inside
+ * the library (each GPU the library runs on holds its own copy from the first
+ * call until the process ends).  The call allocates nothing.
+ *
+ * Arguments, layouts and results are those of attn_fwd_ws (same bits).  The
+ * heads are processed in groups whose V images fit in the buffer, one group
+ * after another on `stream`.  Limit: one head's images, ceil(Skv/64) * 64 * D
+ * * 2 bytes (Skv <= 262144 at D = 128, 524288 at D = 64), must fit, else
+ * DIT_ERR_SCRATCH before anything is launched.
+ *
+ * `stream` must belong to the current device (DIT_ERR_DEVICE otherwise); the
+ * first call on a device looks up that device's buffer address.  Every call
+ * on a GPU uses that GPU's one buffer: calls that may run at the same time
+ * on one GPU (on different streams, or from different threads) race on it
+ * and give undefined results; order them on one stream.
+ */
+#define DIT_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+int attn_fwd_noalloc(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
+                     void *out, float *lse, int B, int H, int Sq, int Skv, int D,
+                     float scale, int causal, int out_dtype, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *dit_attn_status_string(int status);

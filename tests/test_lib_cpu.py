@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dit_attn.h")
 LIB = os.path.join(ROOT, "attention_qk_norm_rope_amd", "libdit_attn.so")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP = range(7)
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP, SCRATCH, DEVICE = range(9)
 BF16, FP32 = 0, 1
 
 
@@ -54,6 +54,7 @@ def lib():
     lib.attn_fwd_varlen.argtypes = [p, p, p, p, i64, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
+    lib.attn_fwd_noalloc.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
     lib.dit_attn_version.restype = ctypes.c_char_p
     return lib
@@ -62,7 +63,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert set(names) == {"qk_norm_rope", "qk_norm_rope_out", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
-                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd",
+                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_fwd_noalloc", "attn_merge", "bsnd_to_bnsd",
                           "bnsd_to_bsnd", "dit_attn_status_string",
                           "dit_attn_version"}, names
     for name in names:
@@ -70,8 +71,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(7):
-        assert lib.dit_attn_status_string(s)
+    for s in range(9):
+        assert lib.dit_attn_status_string(s) != b"unknown status"
     assert lib.dit_attn_status_string(99) == b"unknown status"
     assert b"gfx950" in lib.dit_attn_version()
 
@@ -103,6 +104,21 @@ def test_attn_fwd_rejections(lib):
     assert attn(lib, o=K + 32 * 1024) == ALIAS           # out inside k (k spans 64 KiB)
     assert attn(lib, lse=O + 1024) == ALIAS              # lse inside out
     assert attn(lib, B=1 << 16, H=1 << 16) == SHAPE      # B*H overflows int
+
+
+def test_attn_fwd_noalloc_rejections(lib):
+    f = lib.attn_fwd_noalloc
+    D = 128
+    assert f(None, K, V, 256 * D, O, L, 1, 2, 256, 256, D, 0.125, 0, BF16, None) == NULL
+    assert f(Q, K, V, 256 * D, O, L, 1, 2, 0, 256, D, 0.125, 0, BF16, None) == SHAPE
+    assert f(Q, K, V, 256 * D, O, L, 1, 2, 256, 256, 96, 0.125, 0, BF16, None) == UNSUP
+    assert f(Q + 8, K, V, 256 * D, O, L, 1, 2, 256, 256, D, 0.125, 0, BF16, None) == ALIGN
+    assert f(Q, K, V, 256 * D, Q, L, 1, 2, 256, 256, D, 0.125, 0, BF16, None) == ALIAS
+    # One head's V images (ceil(Skv/64)*64*D*2 bytes) must fit in the 64 MiB
+    # static scratch: 262144 keys fit at D = 128, 262208 do not.
+    big = 262208
+    assert f(Q, K, V, big * D, O, L, 1, 1, 256, big, D, 0.125, 0, BF16, None) == SCRATCH
+    assert f(Q, K, V, 600000 * 64, O, L, 1, 1, 256, 600000, 64, 0.125, 0, FP32, None) == SCRATCH
 
 
 def test_attn_fwd_kv_strided_rejections(lib):
