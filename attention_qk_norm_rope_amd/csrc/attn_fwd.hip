@@ -90,8 +90,7 @@ constexpr int QPW = 32;                // query rows per wave
 constexpr int WAVES = 8;               // waves per workgroup (4 for small grids, workspace path)
 constexpr int SMALL_GRID_ROUNDS = 24;  // causal grids: 4-wave workgroups only below this many 8-wave rounds
 constexpr float LN2 = 0.69314718055994531f;
-constexpr float TAU = 8.0f;            // P <= 2^TAU (log2 units) keeps fp16 P in range and precision
-constexpr float P_SUM_FAST = 256.0f;   // 2^TAU: a lane's tile sum below it bounds each of its P
+constexpr float P_SUM_FAST = 256.0f;   // 2^TAU, TAU = 8: a lane's tile sum below it bounds each of its P
 constexpr int RSRC_WORD3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
 #ifndef DIT_PP_OFFSET
 #define DIT_PP_OFFSET 1
@@ -203,9 +202,15 @@ __device__ __forceinline__ unsigned p_pair(float s0, float s1, float c, float ne
 // store zeros and LSE = -inf.  MERGE: out/lse already hold a partial
 // attention of the same row over other keys; the row is folded into it with
 // the arithmetic of attn_merge (this side in fp32, as an fp32 out_b).
+//
+// vmax (workspace path): per d, the fp32 bits of the largest |v| of this
+// K/V head; the prepared V of a column with largest |v| >= 2^16 was scaled
+// by 2^-e (see v_prep), and its row of O is multiplied back by 2^e here
+// (e = 0, a factor of exactly 1, for every other column).
 template <int D, bool OUT_F32, bool MERGE>
 __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run, float l_half, int64_t orow,
-                                          int64_t lrow, bool valid, bool pad, int hh, void* out, float* lse) {
+                                          int64_t lrow, bool valid, bool pad, int hh, void* out, float* lse,
+                                          const unsigned* vmax) {
     const float l = pair_sum(l_half);
     const bool empty = pad || !(l > 0.f);
     const float inv = empty ? 0.f : 1.0f / l;
@@ -219,9 +224,20 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d = 32 * db + 8 * g + 4 * hh;
+            float sc[4] = {1.f, 1.f, 1.f, 1.f};
+            if (vmax) {
+                const u32x4 mb = *(const u32x4*)(vmax + d);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int x = (int)(mb[i] >> 23);
+                    sc[i] = __builtin_bit_cast(float, (unsigned)(127 + (x >= 143 ? x - 141 : 0)) << 23);
+                }
+            }
             float a[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = empty ? 0.f : o[db][4 * g + i] * inv;   // not 0 * garbage
+            // After the division: o / l is below 2^15 in a scaled column, so
+            // the power of two cannot overflow what the output can hold.
+            for (int i = 0; i < 4; ++i) a[i] = empty ? 0.f : (o[db][4 * g + i] * inv) * sc[i];   // not 0 * garbage
             if constexpr (MERGE) {
                 float x[4];
                 if constexpr (OUT_F32) {
@@ -336,7 +352,8 @@ template <int D, bool OUT_F32, bool FQ, bool VPREP, bool MERGE = false, int W = 
 __global__ void __attribute__((amdgpu_flat_work_group_size(W * 64, W * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                   const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
+                   const uint16_t* __restrict__ vws, const unsigned* __restrict__ vmax, int64_t kv_bh_stride,
+                   void* __restrict__ out,
                    float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
                    int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
                    const int* __restrict__ lkv, int out_heads, int out_h0, int tile0, int halves) {
@@ -617,7 +634,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     const int qi = q0w + n;
     const int64_t lrow = (int64_t)bh * Sq + qi;
     const int64_t orow = out_heads ? ((int64_t)(bh / H) * Sq + qi) * out_heads + out_h0 + bh % H : lrow;
-    store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse);
+    store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse,
+                                 vmax ? vmax + (int64_t)bkv * D : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -641,7 +659,8 @@ template <int D, bool OUT_F32, bool FQ, bool MERGE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-               const uint16_t* __restrict__ vws, int64_t kv_bh_stride, void* __restrict__ out,
+               const uint16_t* __restrict__ vws, const unsigned* __restrict__ vmax, int64_t kv_bh_stride,
+                   void* __restrict__ out,
                float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
                int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
                const int* __restrict__ lkv, int out_heads, int out_h0, int tile0, int halves) {
@@ -900,7 +919,8 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
     const int qi = q0w + n;
     const int64_t lrow = (int64_t)bh * Sq + qi;
     const int64_t orow = out_heads ? ((int64_t)(bh / H) * Sq + qi) * out_heads + out_h0 + bh % H : lrow;
-    store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse);
+    store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse,
+                                 vmax ? vmax + (int64_t)bkv * D : nullptr);
 }
 
 template <int D, bool OUT_F32>
@@ -909,6 +929,9 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
                   const QNormRope* qn, const int* lq, const int* lkv, int out_heads, int out_h0, bool merge,
                   hipStream_t stream) {
     const QNormRope qz{};
+    // The workspace holds the V images, then the largest |v| per (K/V head, d).
+    const unsigned* vmax =
+        vws ? (const unsigned*)((const char*)vws + v_images_bytes(BH / G, Skv, D)) : nullptr;
     // One launch of workgroups of w waves over tiles [tile0, tile0 + ntile)
     // of n_qtiles per head; with halves, every tile of 2*w*QPW rows goes to
     // two workgroups.
@@ -918,7 +941,8 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
         if (nblk > 0x7FFFFFFF || tile0 + ntile > 0x7FFFFFFF) return hipErrorInvalidValue;
         if (nblk == 0) return hipSuccess;
         hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(w * 64), 0, stream, (const uint16_t*)q,
-                           (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)vws, kv_bh_stride, out, lse, Sq,
+                           (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)vws, vmax, kv_bh_stride, out,
+                           lse, Sq,
                            Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, qa, lq, lkv, out_heads, out_h0,
                            (int)tile0, halves ? 1 : 0);
         return hipGetLastError();

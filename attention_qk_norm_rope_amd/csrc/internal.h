@@ -32,7 +32,11 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
                            bool causal, bool out_f32, const void* vws, const QNormRope* qn, const int* lq,
                            const int* lkv, int out_heads, int out_h0, bool merge, hipStream_t stream);
 
-// Bytes of prepared V for BH heads of Skv keys; launch_v_prep writes them.
+// Bytes of prepared V for BH heads of Skv keys; launch_v_prep writes them:
+// v_images_bytes of fp16 V^T tile images, then the fp32 bits of the largest
+// |v| per (head, d) (BH*D unsigned), from which a column's power-of-two scale
+// (applied to the images, undone in the attention epilogue) is derived.
+int64_t v_images_bytes(int64_t BH, int Skv, int D);
 int64_t v_prep_bytes(int64_t BH, int Skv, int D);
 // With lkv != null, head bh (of B*Hkv) keeps keys < lkv[bh / Hkv] and zeros the rest.
 hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D, const int* lkv,

@@ -123,9 +123,11 @@ int qk_norm_rope_out(const void *q_in, const void *k_in, void *q_out, void *k_ou
  * both with fp32 accumulation; the softmax runs in fp32.
  *
  *   q          bf16 [B,H,Sq,D]
- *   k, v       bf16 [B,H,Skv,D]; v must satisfy |v| <= 65504 (its fp16
- *              conversion is exact for |v| in [2^-14, 65504]; smaller
- *              magnitudes keep an absolute accuracy of 2^-25)
+ *   k, v       bf16 [B,H,Skv,D].  Here (no workspace) v must satisfy
+ *              |v| <= 65504: its fp16 conversion is exact for |v| in
+ *              [2^-14, 65504], smaller magnitudes keep an absolute accuracy
+ *              of 2^-25, larger ones overflow.  The workspace entry points
+ *              (attn_fwd_ws and the calls built on it) take any bf16 v.
  *   out        [B,H,Sq,D], bf16 (out_dtype = DIT_BF16) or fp32 (DIT_FP32);
  *              must not overlap q, k, v or lse
  *   lse        fp32 [B,H,Sq], or NULL to skip it
@@ -149,11 +151,15 @@ int attn_fwd_kv_strided(const void *q, const void *k, const void *v, int64_t kv_
 
 /*
  * attn_fwd_kv_strided (same arguments and results) with a caller-provided
- * workspace that lets the kernel stream V without converting it: a first
- * launch writes each 64-key tile of V once as an fp16, transposed tile image
+ * workspace that lets the kernel stream V without converting it: first
+ * launches write each 64-key tile of V once as an fp16, transposed tile image
  * into `workspace`, and the attention launch copies those images straight
- * into LDS.  Faster than attn_fwd on the same inputs; the results are the
- * same arithmetic (identical bits).
+ * into LDS.  Faster than attn_fwd on the same inputs; for |v| <= 65504 the
+ * results are the same arithmetic (identical bits).  Any bf16 v is taken:
+ * a column (head, d) whose largest |v| is 2^16 or more is scaled by an exact
+ * power of two 2^-e into fp16 range before the conversion, and the output's
+ * component d is multiplied back by 2^e (values far below the column's
+ * largest then keep an absolute accuracy of 2^(e-25)).
  *
  *   workspace        device buffer of at least attn_fwd_workspace_bytes(B, H,
  *                    Skv, D) bytes, 16-byte aligned, overlapping no other
@@ -167,8 +173,9 @@ int attn_fwd_ws(const void *q, const void *k, const void *v, int64_t kv_bh_strid
                 int B, int H, int Sq, int Skv, int D, float scale, int causal,
                 int out_dtype, hipStream_t stream);
 
-/* Workspace bytes attn_fwd_ws needs (B*H * ceil(Skv/64) * 64 * D * 2), or -1
- * for arguments attn_fwd_ws would reject. */
+/* Workspace bytes attn_fwd_ws needs (B*H * (ceil(Skv/64) * 64 * D * 2 + D * 4):
+ * the V tile images and the largest |v| of every (head, d)), or -1 for
+ * arguments attn_fwd_ws would reject. */
 int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D);
 
 /*
@@ -333,9 +340,9 @@ int bnsd_to_bsnd(const void *o, void *x, int B, int S, int H, int h0, int Hs, in
  *
  * Arguments, layouts and results are those of attn_fwd_ws (same bits).  The
  * heads are processed in groups whose V images fit in the buffer, one group
- * after another on `stream`.  Limit: one head's images, ceil(Skv/64) * 64 * D
- * * 2 bytes (Skv <= 262144 at D = 128, 524288 at D = 64), must fit, else
- * DIT_ERR_SCRATCH before anything is launched.
+ * after another on `stream`.  Limit: one head's share, ceil(Skv/64) * 64 *
+ * D * 2 + D * 4 bytes (Skv <= 262080 at D = 128, 524224 at D = 64), must
+ * fit, else DIT_ERR_SCRATCH before anything is launched.
  *
  * `stream` must belong to the current device (DIT_ERR_DEVICE otherwise); the
  * first call on a device looks up that device's buffer address.  Every call

@@ -82,7 +82,36 @@ def test_ws_rejects_small_or_misplaced_workspace():
         out = torch.empty((n // 2,), dtype=torch.bfloat16, device=DEV)
         attn_fwd_ws(q, q, q, out, out=out[: B * H * S * D].view(B, H, S, D))
     assert e.value.status == 5
-    np.testing.assert_equal(n, B * H * (S // 64) * 64 * D * 2)
+    np.testing.assert_equal(n, B * H * ((S // 64) * 64 * D * 2 + D * 4))
+
+
+@pytest.mark.parametrize("lo,hi", [(-20.0, 100.0), (60.0, 127.0), (15.0, 16.5)])
+def test_value_range_of_v_workspace_path(lo, hi):
+    """The workspace path takes any bf16 V: magnitudes 2^lo .. 2^hi, beyond
+    fp16's 65504, in every column (so columns are scaled by powers of two
+    before the fp16 conversion and the output is scaled back).  The error is
+    bounded, as below, relative to the largest |v|; with the largest values
+    alone (no smaller ones) the output keeps fp16 precision."""
+    B, H, Sq, Skv, D = 1, 2, 200, 300, 128
+    rng = np.random.default_rng(int(hi))
+    mag = np.exp2(rng.uniform(lo, hi, size=(B, H, Skv, D)))
+    v = inputs.to_bf16_bits(np.where(rng.random(mag.shape) < 0.5, -mag, mag).astype(np.float32))
+    q = inputs.random_bits(98, (B, H, Sq, D))
+    k = inputs.random_bits(99, (B, H, Skv, D))
+    dq, dk, dv = dev_bits(q), dev_bits(k), dev_bits(v)
+    say(f"[attn_ws] value range of v 2^{lo} .. 2^{hi}")
+    o1, l1 = attn_fwd_ws(dq, dk, dv, _ws(B, H, Skv, D), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attn(q, k, v, 1 / math.sqrt(D), False)
+    got = host_f64(o1)
+    vmax = float(np.max(np.abs(inputs.bf16_bits_to_f64(v))))
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref_o))) <= 2.0 ** -10 * vmax
+    assert float(np.max(np.abs(host_f64(l1) - ref_l))) <= 1e-3
+    if hi - lo < 2:
+        # every value within a factor 4 of its column's largest: fp16 relative precision
+        rel = np.abs(got - ref_o) / np.maximum(np.abs(ref_o), 2.0 ** lo)
+        assert float(rel.max()) <= 2.0 ** -9
 
 
 def test_value_range_of_v():

@@ -114,9 +114,10 @@ def test_attn_fwd_noalloc_rejections(lib):
     assert f(Q, K, V, 256 * D, O, L, 1, 2, 256, 256, 96, 0.125, 0, BF16, None) == UNSUP
     assert f(Q + 8, K, V, 256 * D, O, L, 1, 2, 256, 256, D, 0.125, 0, BF16, None) == ALIGN
     assert f(Q, K, V, 256 * D, Q, L, 1, 2, 256, 256, D, 0.125, 0, BF16, None) == ALIAS
-    # One head's V images (ceil(Skv/64)*64*D*2 bytes) must fit in the 64 MiB
-    # static scratch: 262144 keys fit at D = 128, 262208 do not.
-    big = 262208
+    # One head's V images and column maxima (ceil(Skv/64)*64*D*2 + D*4 bytes)
+    # must fit in the 64 MiB static scratch: 262080 keys fit at D = 128,
+    # 262144 do not.
+    big = 262144
     assert f(Q, K, V, big * D, O, L, 1, 1, 256, big, D, 0.125, 0, BF16, None) == SCRATCH
     assert f(Q, K, V, 600000 * 64, O, L, 1, 1, 256, 600000, 64, 0.125, 0, FP32, None) == SCRATCH
 
@@ -131,11 +132,12 @@ def test_attn_fwd_kv_strided_rejections(lib):
 
 def test_attn_fwd_workspace_bytes(lib):
     f = lib.attn_fwd_workspace_bytes
-    # One fp16 image of 64 keys x D per started 64-key tile and head.
-    assert f(1, 2, 256, 64) == 2 * 4 * 64 * 64 * 2
-    assert f(1, 1, 1, 128) == 64 * 128 * 2
-    assert f(2, 3, 65, 128) == 6 * 2 * 64 * 128 * 2
-    assert f(1, 40, 75600, 128) == 40 * 1182 * 64 * 128 * 2
+    # One fp16 image of 64 keys x D per started 64-key tile and head, then
+    # one 4-byte column maximum per (head, d).
+    assert f(1, 2, 256, 64) == 2 * 4 * 64 * 64 * 2 + 2 * 64 * 4
+    assert f(1, 1, 1, 128) == 64 * 128 * 2 + 128 * 4
+    assert f(2, 3, 65, 128) == 6 * 2 * 64 * 128 * 2 + 6 * 128 * 4
+    assert f(1, 40, 75600, 128) == 40 * 1182 * 64 * 128 * 2 + 40 * 128 * 4
     assert f(0, 2, 256, 64) == -1
     assert f(1, 2, 0, 64) == -1
     assert f(1, 2, 256, 96) == -1
@@ -146,7 +148,7 @@ WS = 0x10_0000_0000 * 12
 
 def test_attn_fwd_ws_rejections(lib):
     f = lib.attn_fwd_ws
-    need = 2 * 4 * 64 * 64 * 2
+    need = 2 * 4 * 64 * 64 * 2 + 2 * 64 * 4
 
     def call(ws=WS, nbytes=need, k=K, stride=256 * 64, Skv=256, o=O):
         return f(Q, k, V, stride, ws, nbytes, o, L, 1, 2, 256, Skv, 64, 0.125, 0, BF16, None)
@@ -173,7 +175,7 @@ def test_attn_fwd_gqa_rejections(lib):
     assert call(Hkv=8) == SHAPE                          # more K/V heads than query heads
     assert call(o=None) == NULL
     assert call(stride=255 * 64) == SHAPE
-    need = 2 * 4 * 64 * 64 * 2                           # B*Hkv * 4 tiles * 64 keys * D * 2 B
+    need = 2 * 4 * 64 * 64 * 2 + 2 * 64 * 4              # B*Hkv * (4 tiles * 64 keys * D * 2 B + D * 4 B)
     assert call(ws=WS, nbytes=need - 1) == SHAPE         # sized by Hkv, not H
     assert call(ws=WS + 8, nbytes=need) == ALIGN
     assert call(ws=Q + 4096, nbytes=need) == ALIAS
@@ -184,7 +186,7 @@ TAB = 0x20_0000_0000
 
 def test_attn_fwd_ws_fused_q_rejections(lib):
     f = lib.attn_fwd_ws_fused_q
-    need = 2 * 4 * 64 * 64 * 2
+    need = 2 * 4 * 64 * 64 * 2 + 2 * 64 * 4
     tb = 256 * 64 * 4                                    # one [Sq, D] fp32 table
 
     def call(ws=WS, w=TAB, cq=TAB + 4096, sq=TAB + 4096 + tb, eps=1e-6, o=O):
@@ -205,7 +207,7 @@ def test_attn_fwd_ws_fused_q_rejections(lib):
 
 def test_attn_fwd_ws_bsnd_rejections(lib):
     f = lib.attn_fwd_ws_bsnd
-    need = 2 * 4 * 64 * 64 * 2
+    need = 2 * 4 * 64 * 64 * 2 + 2 * 64 * 4
     # B1, H2, Sq = Skv = 256, D64 into a BSND output of `heads` heads.
 
     def call(heads=6, h0=2, ws=WS, o=O, dt=BF16, lse=L):
@@ -226,7 +228,7 @@ def test_attn_fwd_ws_bsnd_rejections(lib):
 
 def test_attn_fwd_ws_merge_rejections(lib):
     f = lib.attn_fwd_ws_merge
-    need = 2 * 4 * 64 * 64 * 2
+    need = 2 * 4 * 64 * 64 * 2 + 2 * 64 * 4
 
     def call(ws=WS, o=O, lse=L, dt=FP32, nbytes=need):
         return f(Q, K, V, 256 * 64, ws, nbytes, o, lse, 1, 2, 256, 256, 64, 0.125, 0, dt, None)
