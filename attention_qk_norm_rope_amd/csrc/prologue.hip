@@ -25,11 +25,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Grid: x = blocks of RPB sequence positions, y = q or k, z = groups of HB
 // heads.  A thread loads the cos/sin/weight values of its row slice once and
-// applies them to the same position of HB heads (8 rows in flight), so the
-// tables (shared by every (b,h)) are read once per HB heads instead of once
-// per row.
-constexpr int HB = 40;       // (b,h) rows per thread
-constexpr int UNR = 8;       // rows in flight per thread
+// applies them to the same position of HB heads (all HB rows in flight), so
+// the tables (shared by every (b,h)) are read once per HB heads instead of
+// once per row.  HB trades table reads against the number of blocks in
+// flight; q and k are read and written once, with non-temporal accesses.
+constexpr int HB = 10;       // (b,h) rows per thread
+constexpr int UNR = 10;      // rows in flight per thread
 
 template <int D>
 __global__ void __launch_bounds__(256)
@@ -73,7 +74,7 @@ qk_norm_rope_kernel(const uint16_t* q_src, const uint16_t* k_src, uint16_t* q_ds
         u32x4 raw[UNR];
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
-            if (bh + u < bh1) raw[u] = *(const u32x4*)(x + ((int64_t)(bh + u) * S + s) * D + d0);
+            if (bh + u < bh1) raw[u] = __builtin_nontemporal_load((const u32x4*)(x + ((int64_t)(bh + u) * S + s) * D + d0));
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             if (bh + u >= bh1) break;
@@ -90,7 +91,7 @@ qk_norm_rope_kernel(const uint16_t* q_src, const uint16_t* k_src, uint16_t* q_ds
             for (int i = 0; i < 4; ++i)
                 res[i] = nr::pair(xv[2 * i], xv[2 * i + 1], inv_r, wv[2 * i], wv[2 * i + 1], cv[2 * i],
                                   cv[2 * i + 1], sv[2 * i], sv[2 * i + 1]);
-            *(u32x4*)(y + ((int64_t)(bh + u) * S + s) * D + d0) = res;
+            __builtin_nontemporal_store(res, (u32x4*)(y + ((int64_t)(bh + u) * S + s) * D + d0));
         }
     }
     }
