@@ -9,7 +9,7 @@ library on first use and raise if it is missing.
 from __future__ import annotations
 
 __all__ = ["qk_norm_rope", "qk_norm_rope_out", "attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_merge",
-           "attn_fwd_ring_overlap", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_fwd_noalloc", "bsnd_to_bnsd", "bnsd_to_bsnd",
+           "attn_fwd_ring_overlap", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_fwd_noalloc", "attn_fwd_launch_form", "bsnd_to_bnsd", "bnsd_to_bsnd",
            "status_string", "version", "library_path"]
 
 

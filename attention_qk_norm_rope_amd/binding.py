@@ -50,6 +50,7 @@ def _load():
     lib.attn_fwd_gqa.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, i32, f32, i32, i32, p]
     lib.attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_fwd_workspace_bytes.restype = i64
+    lib.attn_fwd_launch_form.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i64, p, ctypes.POINTER(i32)]
     lib.attn_fwd_ws_fused_q.argtypes = [p, p, p, i64, p, i64, p, p, p, p, p, f32, i32, i32, i32, i32, i32, f32, i32,
                                         i32, p]
     lib.attn_fwd_ws_bsnd.argtypes = [p, p, p, i64, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, p]
@@ -61,7 +62,7 @@ def _load():
     lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     for name in ("qk_norm_rope", "qk_norm_rope_out", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws", "attn_fwd_gqa", "attn_fwd_ws_fused_q",
                  "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_merge", "bsnd_to_bnsd", "bnsd_to_bsnd",
-                 "attn_fwd_noalloc"):
+                 "attn_fwd_noalloc", "attn_fwd_launch_form"):
         getattr(lib, name).restype = i32
     lib.dit_attn_status_string.argtypes = [i32]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
@@ -263,12 +264,30 @@ def attn_fwd_workspace_bytes(B: int, H: int, Skv: int, D: int) -> int:
     return n
 
 
+FORMS = {0: "one", 1: "halves", 2: "split", 3: "all4"}
+
+
+def attn_fwd_launch_form(B: int, H: int, Sq: int, Skv: int, D: int, causal: bool = False,
+                         workspace_bytes: int = 0, Hkv: int | None = None, varlen: bool = False) -> str:
+    """Launch form ("one", "halves", "split" or "all4") that an attention call
+    with these sizes takes on the current device; workspace_bytes = 0 for a
+    call without a workspace."""
+    form = ctypes.c_int(-1)
+    st = _load().attn_fwd_launch_form(int(B), int(H), int(H if Hkv is None else Hkv), int(Sq), int(Skv), int(D),
+                                      1 if causal else 0, 1 if varlen else 0, int(workspace_bytes), _stream(),
+                                      ctypes.byref(form))
+    _check("attn_fwd_launch_form", st)
+    return FORMS[form.value]
+
+
 def attn_fwd_ws(q, k, v, workspace, out=None, lse=None, scale: float | None = None,
                 causal: bool = False, out_dtype=torch.bfloat16, return_lse: bool = True):
-    """attn_fwd with a caller-owned device workspace (a contiguous tensor of
-    at least attn_fwd_workspace_bytes(B, H, Skv, D) bytes, any dtype).  Same
-    results as attn_fwd, faster: V is first rewritten into the workspace in
-    the kernel's tile layout.  The workspace holds scratch afterwards."""
+    """attn_fwd with a caller-owned device workspace (a contiguous tensor,
+    any dtype, of attn_fwd_workspace_bytes(B, H, Skv, D) bytes, or of at least
+    the V part B*H*(ceil(Skv/64)*64*D*2 + D*4) bytes, which rules out the split
+    launch).  Same results as attn_fwd, faster: V is first rewritten into the
+    workspace in the kernel's tile layout.  The workspace holds scratch
+    afterwards."""
     (B, H, Sq, Skv, D), sk, scale, out, lse = _attn_args(q, k, v, out, lse, scale, out_dtype, return_lse)
     if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")

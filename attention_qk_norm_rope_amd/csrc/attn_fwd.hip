@@ -67,6 +67,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace dit {
@@ -89,9 +91,12 @@ constexpr int BN = 64;                 // keys per tile
 constexpr int QPW = 32;                // query rows per wave
 constexpr int WAVES = 8;               // waves per workgroup (4 for small grids, workspace path)
 constexpr int SMALL_GRID_ROUNDS = 24;  // causal grids: 4-wave workgroups only below this many 8-wave rounds
+constexpr int SK_MIN_ITERS = 16;       // split launch: key tiles per workgroup at least
+constexpr int SK_LAUNCH_COST = 40;     // split launch: measured fixed cost, in key tiles of one workgroup
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float P_SUM_FAST = 256.0f;   // 2^TAU, TAU = 8: a lane's tile sum below it bounds each of its P
 constexpr int RSRC_WORD3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
+constexpr int CPOL_SC1 = 16;           // buffer access cache policy: coherent across the device's L2s
 #ifndef DIT_PP_OFFSET
 #define DIT_PP_OFFSET 1
 #endif
@@ -151,10 +156,40 @@ __device__ __forceinline__ int kv_head(int bh, int H, int G) {
     return G == 1 ? bh : (bh / H) * (H / G) + (bh % H) / G;
 }
 
-// Workgroup id -> logical tile id, so that each XCD owns a contiguous range.
-__device__ __forceinline__ int xcd_remap(int wid, int nblk) {
-    const int per = nblk >> 3, rem = nblk & 7, xcd = wid & 7;
-    return xcd * per + min(xcd, rem) + (wid >> 3);
+// Workgroup id -> logical tile id, so that each XCD owns a contiguous range
+// (the dispatcher deals workgroup ids round-robin over the nx XCDs).
+__device__ __forceinline__ int xcd_remap(int wid, int nblk, int nx) {
+    if (nx <= 1) return wid;
+    const int per = nblk / nx, rem = nblk % nx, xcd = wid % nx;
+    return xcd * per + min(xcd, rem) + wid / nx;
+}
+
+// Split-key launch (full attention over the workspace).  The query tiles of
+// a last, partly filled round of workgroups are cut along the keys into
+// `units` equal shares of consecutive (query tile, key tile) iterations, one
+// share per workgroup of a launch of its own, so every CU gets the same
+// number of key tiles.  A query tile that several shares cover leaves each
+// piece's normalised rows and LSE in a slot; the workgroup that completes the
+// tile's last piece folds the pieces in share order with the arithmetic of
+// attn_merge (merge_math.h).
+struct SplitK {
+    int* cnt;           // [tiles] pieces completed per split query tile; zero at launch
+    float* part_l;      // [2 * units][256] LSE of the partial pieces
+    float* part_o;      // [2 * units][256][D] their O / l in fp32
+    int64_t iters;      // key tiles over all split query tiles (tiles * nkt)
+    int units;          // workgroups of the launch (<= SK_MAX_UNITS)
+    int nkt;            // key tiles per query tile
+};
+// Share u covers iterations [u * iters / units, (u + 1) * iters / units).
+__device__ __forceinline__ int64_t sk_start(int u, const SplitK& sk) { return (int64_t)u * sk.iters / sk.units; }
+// The share that holds iteration x.
+__device__ __forceinline__ int sk_unit(int64_t x, const SplitK& sk) {
+    return (int)(((x + 1) * sk.units - 1) / sk.iters);
+}
+// A share has at most two partial pieces: the one it starts with (slot 2u)
+// and the one it ends with (slot 2u + 1).
+__device__ __forceinline__ int sk_slot(int u, int tl, const SplitK& sk) {
+    return 2 * u + (sk_start(u, sk) / sk.nkt != tl ? 1 : 0);
 }
 
 // Ragged key tail and causal diagonal of the tile starting at kv0, for the
@@ -266,6 +301,123 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run
     if (lse && hh == 0) lse[lrow] = lm;
 }
 
+// Partial rows of the split launch are written and read with the cache
+// policy of agent-scope atomic stores and loads (sc1): those accesses are
+// coherent across the L2s of the device's XCDs, so a piece finished on one
+// XCD is seen by the workgroup that folds it on another without an L2-wide
+// write-back or invalidate.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc_l(const SplitK& sk) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)sk.part_l, (short)0, 2 * SK_MAX_UNITS * WAVES * QPW * 4,
+                                             RSRC_WORD3);
+}
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc_o(const SplitK& sk) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)sk.part_o, (short)0, 2 * SK_MAX_UNITS * WAVES * QPW * D * 4,
+                                             RSRC_WORD3);
+}
+
+// Row prow of a partial slot: O / l (with the column scales of store_row)
+// and the LSE, as store_row stores an fp32 row.
+template <int D>
+__device__ __forceinline__ void sk_store_partial(const f32x16 (&o)[D / 32], float m_run, float l_half, int prow,
+                                                 bool pad, int hh, const SplitK& sk, const unsigned* vmax) {
+    const float l = pair_sum(l_half);
+    const bool empty = pad || !(l > 0.f);
+    const float inv = empty ? 0.f : 1.0f / l;
+    const float lb = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l)) * LN2;
+    const __amdgpu_buffer_rsrc_t rl = sk_rsrc_l(sk), ro = sk_rsrc_o<D>(sk);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = 32 * db + 8 * g + 4 * hh;
+            float sc[4] = {1.f, 1.f, 1.f, 1.f};
+            if (vmax) {
+                const u32x4 mb = *(const u32x4*)(vmax + d);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int x = (int)(mb[i] >> 23);
+                    sc[i] = __builtin_bit_cast(float, (unsigned)(127 + (x >= 143 ? x - 141 : 0)) << 23);
+                }
+            }
+            f32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = empty ? 0.f : (o[db][4 * g + i] * inv) * sc[i];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (prow * D + d) * 4, 0,
+                                                   CPOL_SC1);
+        }
+    if (hh == 0) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lb), rl, prow * 4, 0, CPOL_SC1);
+}
+
+// Split launch: fold the partial pieces of split tile tl (shares u0..u1, in
+// that order) for row r of the tile and store the row as store_row would
+// (with MERGE, into the running out/lse).  Each fold is the two-way merge of
+// attn_merge with the fp32 result so far as side a and the next piece as
+// side b; the lane keeps the same d values as in store_row.
+template <int D, bool OUT_F32, bool MERGE>
+__device__ __forceinline__ void sk_finish(const SplitK& sk, int tl, int u0, int u1, int r, int hh, int64_t orow,
+                                          int64_t lrow, bool valid, void* out, float* lse) {
+    constexpr int ROWS = WAVES * QPW;
+    if (!valid) return;
+    const __amdgpu_buffer_rsrc_t rl = sk_rsrc_l(sk), ro = sk_rsrc_o<D>(sk);
+    // One piece at a time: loading the next piece ahead costs registers that
+    // the split kernel's main loop then spills.
+    float acc[D / 32][16];
+    float la = -INFINITY;
+    for (int u = u0; u <= u1; ++u) {
+        const int prow = sk_slot(u, tl, sk) * ROWS + r;
+        const float lb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, prow * 4, 0, CPOL_SC1));
+        float wa = 0.f, wb = 0.f, lm = lb;
+        if (u > u0) mg::weights(la, lb, wa, wb, lm);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    ro, (prow * D + 32 * db + 8 * g + 4 * hh) * 4, 0, CPOL_SC1));
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[db][4 * g + i] = u == u0 ? x[i] : mg::combine(wa, acc[db][4 * g + i], wb, x[i]);
+            }
+        la = lm;
+    }
+    float wa = 0.f, wb = 0.f, lm = la;
+    if constexpr (MERGE) mg::weights(lse[lrow], la, wa, wb, lm);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = 32 * db + 8 * g + 4 * hh;
+            float a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = acc[db][4 * g + i];
+            if constexpr (MERGE) {
+                float x[4];
+                if constexpr (OUT_F32) {
+                    const f32x4 rd = *(const f32x4*)((const float*)out + orow * D + d);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = rd[i];
+                } else {
+                    const u32x2 rd = *(const u32x2*)((const uint16_t*)out + orow * D + d);
+                    x[0] = __builtin_bit_cast(float, rd[0] << 16);
+                    x[1] = __builtin_bit_cast(float, rd[0] & 0xFFFF0000u);
+                    x[2] = __builtin_bit_cast(float, rd[1] << 16);
+                    x[3] = __builtin_bit_cast(float, rd[1] & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = mg::combine(wa, x[i], wb, a[i]);
+            }
+            if constexpr (OUT_F32) {
+                f32x4 w = {a[0], a[1], a[2], a[3]};
+                *(f32x4*)((float*)out + orow * D + d) = w;
+            } else {
+                u32x2 w = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])};
+                *(u32x2*)((uint16_t*)out + orow * D + d) = w;
+            }
+        }
+    if (lse && hh == 0) lse[lrow] = lm;
+}
+
 // Q fragments of query row qi (lane half hh): qf[t] holds elements
 // 16t + 8hh .. +7 of the row, the B operand of the score MFMA of k-step t.
 // FQ: the row is raw and gets the RMSNorm + rotary of qk_norm_rope on the way
@@ -356,7 +508,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
                    void* __restrict__ out,
                    float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
                    int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
-                   const int* __restrict__ lkv, int out_heads, int out_h0, int tile0, int halves) {
+                   const int* __restrict__ lkv, int out_heads, int out_h0, int tile0, int halves, int nxcd,
+                   SplitK) {
     static_assert(W == WAVES || (W == 4 && VPREP), "4-wave workgroups read V from the workspace only");
     constexpr int BM = W * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
@@ -374,7 +527,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     // Tile of this workgroup: logical tile tile0 + id of n_qtiles tiles per
     // head; with halves, two consecutive workgroups split one tile of 2*BM
     // rows (the tail of a grid of larger workgroups).
-    int logical = xcd_remap(blockIdx.x, gridDim.x);
+    int logical = xcd_remap(blockIdx.x, gridDim.x, nxcd);
     int half = 0;
     if (halves) {
         half = logical & 1;
@@ -655,7 +808,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 // The DMAs of K_{j+2} and V_{j+1} are issued in the phase pair that starts
 // with group 0's M(j); each wave waits for its own part of them two phases
 // later (vmcnt), and they are read after the barrier that follows.
-template <int D, bool OUT_F32, bool FQ, bool MERGE>
+template <int D, bool OUT_F32, bool FQ, bool MERGE, bool SK = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -663,7 +816,8 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
                    void* __restrict__ out,
                float* __restrict__ lse, int Sq, int Skv_all, float c, unsigned qsign, int causal,
                int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
-               const int* __restrict__ lkv, int out_heads, int out_h0, int tile0, int halves) {
+               const int* __restrict__ lkv, int out_heads, int out_h0, int tile0, int halves, int nxcd,
+               SplitK sk) {
     constexpr int W = 8;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int TILE = BN * D;
@@ -691,302 +845,444 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
         if constexpr (b == 0) return Vt0; else if constexpr (b == 1) return Vt1; else return Vt2;
     };
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x) + tile0;
-    const int bh = logical / n_qtiles;
-    const int bkv = kv_head(bh, H, G);
-    const int Sq_b = lq ? min(max(lq[bh / H], 0), Sq) : Sq;
-    const int Skv = lkv ? min(max(lkv[bh / H], 0), Skv_all) : Skv_all;
-    const int q0 = (logical - bh * n_qtiles) * (W * QPW);
-
+    __shared__ int sk_arrived;
     const int tid = threadIdx.x;
     const int wave = uniform_int(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
     const int grp = wave >> 2;
-    const int q0w = q0 + wave * QPW;
-    const int n_vt = (Skv_all + BN - 1) / BN;
+    const int n_vt_all = (Skv_all + BN - 1) / BN;
 
-    bf16x8 qf[DT];
-    load_q<D, FQ>(q + (int64_t)bh * Sq * D, Sq, q0w + n, hh, qsign, qn, qf);
+    // One piece of work: query tile `logical` against key tiles [kt0, kt1)
+    // (kt1 < 0: all keys of the batch).  slot < 0: the rows go to out;
+    // otherwise to partial slot `slot` of split tile tl.
+    auto piece = [&](int logical, int kt0, int kt1, int slot, int tl) __attribute__((always_inline)) {
+        const int bh = logical / n_qtiles;
+        const int bkv = kv_head(bh, H, G);
+        const int Sq_b = lq ? min(max(lq[bh / H], 0), Sq) : Sq;
+        const int Skv_b = lkv ? min(max(lkv[bh / H], 0), Skv_all) : Skv_all;
+        const int q0 = (logical - bh * n_qtiles) * (W * QPW);
+        const int q0w = q0 + wave * QPW;
+        const int kt_end = kt1 < 0 ? (Skv_b + BN - 1) / BN : kt1;
+        // Keys of the piece, counted from key kt0 * BN, and its V image tiles
+        // (those past them read as zeros).
+        const int Skv = min(Skv_b, kt_end * BN) - kt0 * BN;
+        const int n_vt = kt1 < 0 ? n_vt_all : kt_end - kt0;
 
-    const int n_tiles = q0 >= Sq_b ? 0 : (Skv + BN - 1) / BN;
+        bf16x8 qf[DT];
+        load_q<D, FQ>(q + (int64_t)bh * Sq * D, Sq, q0w + n, hh, qsign, qn, qf);
 
-    const uint16_t* kbh = k + (int64_t)bkv * kv_bh_stride;
-    auto dma_k = [&](int tile, auto b) {
-        const int kv0 = tile * BN;
-        const int left = Skv - kv0;
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(kbh + (int64_t)kv0 * D), (short)0, left > 0 ? left * D * 2 : 0, RSRC_WORD3);
-#pragma unroll
-        for (int i = 0; i < KDMA; ++i) {
-            const int s = (wave * KDMA + i) * 64 + lane;
-            const int key = s / SL;
-            const int slot = (s % SL) ^ kswz<D>(key);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Kbuf(b) + (wave * KDMA + i) * 512), 16,
-                                                     (key * D + 8 * slot) * 2, 0, 0, 0);
-        }
-    };
-    const uint16_t* vbh = vws + (int64_t)bkv * n_vt * TILE;
-    auto dma_v = [&](int tile, auto b) {
-        // Tiles past the image read as zeros.
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(vbh + (int64_t)min(tile, n_vt - 1) * TILE), (short)0, tile < n_vt ? TILE * 2 : 0, RSRC_WORD3);
-#pragma unroll
-        for (int i = 0; i < KDMA; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Vbuf(b) + (wave * KDMA + i) * 512), 16,
-                                                     ((wave * KDMA + i) * 64 + lane) * 16, 0, 0, 0);
-    };
-    auto kfrag = [&](auto b, int kb, int t) {
-        const int key = 32 * kb + n;
-        const int slot = (2 * t + hh) ^ kswz<D>(key);
-        return __builtin_bit_cast(bf16x8, *(const u32x4*)(Kbuf(b) + key * D + 8 * slot));
-    };
-    auto vfrag = [&](auto b, int kb, int u, int db) {
-        const int row = 32 * db + n;
-        const int lslot = 4 * kb + 2 * u + hh;
-        return __builtin_bit_cast(f16x8, *(const u32x4*)(Vbuf(b) + row * BN + 8 * (lslot ^ ((row >> 1) & 7))));
-    };
-    // Step i of a phase M: score MFMA (kb = i % KB, k-step i / KB) and
-    // P V MFMA (index i = db + DB (u + 2 kb)).
-    auto pv_idx = [](int i, int& kb, int& u, int& db) {
-        kb = i / (2 * DB);
-        u = (i / DB) % 2;
-        db = i % DB;
-    };
-    auto barrier = []() { asm volatile("s_barrier" ::: "memory"); };
+        const int n_tiles = q0 >= Sq_b || Skv <= 0 ? 0 : (Skv + BN - 1) / BN;
 
-    f32x16 o[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16 s[KB];
-    f16x8 p[KB][2];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) p[kb][u] = f16x8{};
-    bf16x8 kf[NR];
-    f16x8 vf[NR];
-
-    // Fragments of step i of phase M(j): K_j in buffer bj, V_{j-1} in bv.
-    auto load_step = [&](auto bj, auto bv, int i) {
-        int kb, u, db;
-        pv_idx(i, kb, u, db);
-        kf[i % NR] = kfrag(bj, i % KB, i / KB);
-        vf[i % NR] = vfrag(bv, kb, u, db);
-    };
-
-    // Prologue: K_0, K_1, V_0 by DMA; zeros in the buffer of V_{-1} (tile -1
-    // mod 3 = 2), which P_{-1} = 0 multiplies in M(0).
-    dma_k(0, B0{});
-    dma_k(1, B1{});
-    dma_v(0, B0{});
-#pragma unroll
-    for (int i = 0; i < TILE / (W * 512); ++i)
-        *(u32x4*)(Vt2 + (i * W * 64 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-    barrier();
-
-    using B2 = std::integral_constant<int, 2>;
-#pragma unroll
-    for (int i = 0; i < PF; ++i) load_step(B0{}, B2{}, i);
-
-    // One tile: M(j) then V(j) of group GRP.  b = j mod 3 selects the buffers.
-    // Each group runs its own copy of the loop, so the DMAs sit at fixed
-    // points of each copy (the compiler then sees which are in flight).
-    auto tile_step = [&](auto gc, auto bc, int j) __attribute__((always_inline)) {
-        constexpr int GRP = decltype(gc)::value;
-        constexpr int b = decltype(bc)::value;
-        using BK = std::integral_constant<int, b>;             // K_j
-        using BV = std::integral_constant<int, (b + 2) % 3>;   // V_{j-1}
-        using BN1 = std::integral_constant<int, (b + 1) % 3>;  // K_{j+1}, V_{j+1}
-        using BN2 = std::integral_constant<int, (b + 2) % 3>;  // K_{j+2}
-        // ---- M(j)
-        if constexpr (GRP == 0 || GRP == 2) {
-            dma_k(j + 2, BN2{});
-            dma_v(j + 1, BN1{});
-        }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-        if constexpr (PP_PRIO) __builtin_amdgcn_s_setprio(1);
-        // Step i: the fragment reads of step i + PF, then the two MFMAs of
-        // step i (fenced, so the reads stay PF steps ahead).
-#pragma unroll
-        for (int i = 0; i < NSTEP; ++i) {
-            if (i + PF < NSTEP) load_step(BK{}, BV{}, i + PF);
-            int kb, u, db;
-            pv_idx(i, kb, u, db);
-            s[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % NR], qf[i / KB], s[i % KB], 0, 0, 0);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % NR], p[kb][u], o[db], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (PP_PRIO) __builtin_amdgcn_s_setprio(0);
-        // Group 0: its DMAs of the phase pair before have landed (one batch,
-        // issued at the start of this phase, stays in flight).
-        if constexpr (GRP == 0) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);
-        if constexpr (GRP != 2) barrier();
-        // ---- V(j)
-        if constexpr (GRP == 1) {
-            dma_k(j + 3, BK{});
-            dma_v(j + 2, BN2{});
-        }
-        const int kv0 = j * BN;
-        if (kv0 + BN > Skv) mask_tile(s, kv0, Skv, false, 0, hh);
-        // Softmax of the tile (the same rule as attn_fwd_kernel, see there).
-        float alpha = 1.0f, lsum = 0.f;
-        bool grow = false;
-        u32x4 w4[KB][2];
-        auto make_p = [&](float neg_m) __attribute__((always_inline)) {
-            lsum = 0.f;
-#pragma unroll
-            for (int unit = 0; unit < 16; ++unit) {
-                const int kb = unit / 8, u = (unit / 4) % 2, e = unit % 4;
-                w4[kb][u][e] = p_pair(s[kb][8 * u + 2 * e], s[kb][8 * u + 2 * e + 1], c, neg_m, lsum);
+        const uint16_t* kbh = k + (int64_t)bkv * kv_bh_stride + (int64_t)kt0 * BN * D;
+        auto dma_k = [&](int tile, auto b) {
+            const int kv0 = tile * BN;
+            const int left = Skv - kv0;
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(kbh + (int64_t)kv0 * D), (short)0, left > 0 ? left * D * 2 : 0, RSRC_WORD3);
+    #pragma unroll
+            for (int i = 0; i < KDMA; ++i) {
+                const int s = (wave * KDMA + i) * 64 + lane;
+                const int key = s / SL;
+                const int slot = (s % SL) ^ kswz<D>(key);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Kbuf(b) + (wave * KDMA + i) * 512), 16,
+                                                         (key * D + 8 * slot) * 2, 0, 0, 0);
             }
         };
-        make_p(-m_run);
-        if (!__all(lsum < P_SUM_FAST)) {
-            tile_max(s, c, 0.f, m_run, alpha, grow);
-            if (grow) make_p(-m_run);
-        }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) p[kb][u] = __builtin_bit_cast(f16x8, w4[kb][u]);
-        l_run = __builtin_fmaf(l_run, alpha, lsum);
-        if (__any(grow && l_run >= 0.f)) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        }
-        // First fragments of M(j+1): K_{j+1}, and V_j (buffer b).
-#pragma unroll
-        for (int i = 0; i < PF; ++i) load_step(BN1{}, BK{}, i);
-        if constexpr (GRP == 1) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);   // its DMAs of the pair before
-        if constexpr (GRP == 2) __builtin_amdgcn_s_waitcnt(0x0F70);           // this tile's DMAs have landed
-        barrier();
-    };
+        const uint16_t* vbh = vws + ((int64_t)bkv * n_vt_all + kt0) * TILE;
+        auto dma_v = [&](int tile, auto b) {
+            // Tiles past the image read as zeros.
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(vbh + (int64_t)min(tile, n_vt - 1) * TILE), (short)0, tile < n_vt ? TILE * 2 : 0, RSRC_WORD3);
+    #pragma unroll
+            for (int i = 0; i < KDMA; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Vbuf(b) + (wave * KDMA + i) * 512), 16,
+                                                         ((wave * KDMA + i) * 64 + lane) * 16, 0, 0, 0);
+        };
+        auto kfrag = [&](auto b, int kb, int t) {
+            const int key = 32 * kb + n;
+            const int slot = (2 * t + hh) ^ kswz<D>(key);
+            return __builtin_bit_cast(bf16x8, *(const u32x4*)(Kbuf(b) + key * D + 8 * slot));
+        };
+        auto vfrag = [&](auto b, int kb, int u, int db) {
+            const int row = 32 * db + n;
+            const int lslot = 4 * kb + 2 * u + hh;
+            return __builtin_bit_cast(f16x8, *(const u32x4*)(Vbuf(b) + row * BN + 8 * (lslot ^ ((row >> 1) & 7))));
+        };
+        // Step i of a phase M: score MFMA (kb = i % KB, k-step i / KB) and
+        // P V MFMA (index i = db + DB (u + 2 kb)).
+        auto pv_idx = [](int i, int& kb, int& u, int& db) {
+            kb = i / (2 * DB);
+            u = (i / DB) % 2;
+            db = i % DB;
+        };
+        auto barrier = []() { asm volatile("s_barrier" ::: "memory"); };
 
-    // Last P V: O += V_{n-1}^T P_{n-1}^T, V_{n-1} in buffer (n-1) mod 3; its
-    // first fragments were loaded at the end of V(n-1) (with the unused K
-    // fragments of a tile past the end).
-    auto last_pv = [&](auto bv) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NSTEP; ++i) {
+        f32x16 o[DB];
+    #pragma unroll
+        for (int db = 0; db < DB; ++db)
+    #pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x16 s[KB];
+        f16x8 p[KB][2];
+    #pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+    #pragma unroll
+            for (int u = 0; u < 2; ++u) p[kb][u] = f16x8{};
+        bf16x8 kf[NR];
+        f16x8 vf[NR];
+
+        // Fragments of step i of phase M(j): K_j in buffer bj, V_{j-1} in bv.
+        auto load_step = [&](auto bj, auto bv, int i) {
             int kb, u, db;
             pv_idx(i, kb, u, db);
-            const f16x8 vv = i < PF ? vf[i % NR] : vfrag(bv, kb, u, db);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, p[kb][u], o[db], 0, 0, 0);
-        }
-    };
+            kf[i % NR] = kfrag(bj, i % KB, i / KB);
+            vf[i % NR] = vfrag(bv, kb, u, db);
+        };
 
-    auto run = [&](auto gc) __attribute__((always_inline)) {
-        constexpr int GRP = decltype(gc)::value;
-        if constexpr (GRP == 1) {
-            // Group 1 idles for the first phase; it issues its part of the
-            // DMAs of the first phase pair (K_2, V_1) there.
-            dma_k(2, B2{});
-            dma_v(1, B1{});
+        // Prologue: K_0, K_1, V_0 by DMA; zeros in the buffer of V_{-1} (tile -1
+        // mod 3 = 2), which P_{-1} = 0 multiplies in M(0).
+        dma_k(0, B0{});
+        dma_k(1, B1{});
+        dma_v(0, B0{});
+    #pragma unroll
+        for (int i = 0; i < TILE / (W * 512); ++i)
+            *(u32x4*)(Vt2 + (i * W * 64 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        barrier();
+
+        using B2 = std::integral_constant<int, 2>;
+    #pragma unroll
+        for (int i = 0; i < PF; ++i) load_step(B0{}, B2{}, i);
+
+        // One tile: M(j) then V(j) of group GRP.  b = j mod 3 selects the buffers.
+        // Each group runs its own copy of the loop, so the DMAs sit at fixed
+        // points of each copy (the compiler then sees which are in flight).
+        auto tile_step = [&](auto gc, auto bc, int j) __attribute__((always_inline)) {
+            constexpr int GRP = decltype(gc)::value;
+            constexpr int b = decltype(bc)::value;
+            using BK = std::integral_constant<int, b>;             // K_j
+            using BV = std::integral_constant<int, (b + 2) % 3>;   // V_{j-1}
+            using BN1 = std::integral_constant<int, (b + 1) % 3>;  // K_{j+1}, V_{j+1}
+            using BN2 = std::integral_constant<int, (b + 2) % 3>;  // K_{j+2}
+            // ---- M(j)
+            if constexpr (GRP == 0 || GRP == 2) {
+                dma_k(j + 2, BN2{});
+                dma_v(j + 1, BN1{});
+            }
+    #pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+            if constexpr (PP_PRIO) __builtin_amdgcn_s_setprio(1);
+            // Step i: the fragment reads of step i + PF, then the two MFMAs of
+            // step i (fenced, so the reads stay PF steps ahead).
+    #pragma unroll
+            for (int i = 0; i < NSTEP; ++i) {
+                if (i + PF < NSTEP) load_step(BK{}, BV{}, i + PF);
+                int kb, u, db;
+                pv_idx(i, kb, u, db);
+                s[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % NR], qf[i / KB], s[i % KB], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % NR], p[kb][u], o[db], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (PP_PRIO) __builtin_amdgcn_s_setprio(0);
+            // Group 0: its DMAs of the phase pair before have landed (one batch,
+            // issued at the start of this phase, stays in flight).
+            if constexpr (GRP == 0) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);
+            if constexpr (GRP != 2) barrier();
+            // ---- V(j)
+            if constexpr (GRP == 1) {
+                dma_k(j + 3, BK{});
+                dma_v(j + 2, BN2{});
+            }
+            const int kv0 = j * BN;
+            if (kv0 + BN > Skv) mask_tile(s, kv0, Skv, false, 0, hh);
+            // Softmax of the tile (the same rule as attn_fwd_kernel, see there).
+            float alpha = 1.0f, lsum = 0.f;
+            bool grow = false;
+            u32x4 w4[KB][2];
+            auto make_p = [&](float neg_m) __attribute__((always_inline)) {
+                lsum = 0.f;
+    #pragma unroll
+                for (int unit = 0; unit < 16; ++unit) {
+                    const int kb = unit / 8, u = (unit / 4) % 2, e = unit % 4;
+                    w4[kb][u][e] = p_pair(s[kb][8 * u + 2 * e], s[kb][8 * u + 2 * e + 1], c, neg_m, lsum);
+                }
+            };
+            make_p(-m_run);
+            if (!__all(lsum < P_SUM_FAST)) {
+                tile_max(s, c, 0.f, m_run, alpha, grow);
+                if (grow) make_p(-m_run);
+            }
+    #pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+    #pragma unroll
+                for (int u = 0; u < 2; ++u) p[kb][u] = __builtin_bit_cast(f16x8, w4[kb][u]);
+            l_run = __builtin_fmaf(l_run, alpha, lsum);
+            if (__any(grow && l_run >= 0.f)) {
+    #pragma unroll
+                for (int db = 0; db < DB; ++db)
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+            }
+            // First fragments of M(j+1): K_{j+1}, and V_j (buffer b).
+    #pragma unroll
+            for (int i = 0; i < PF; ++i) load_step(BN1{}, BK{}, i);
+            if constexpr (GRP == 1) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);   // its DMAs of the pair before
+            if constexpr (GRP == 2) __builtin_amdgcn_s_waitcnt(0x0F70);           // this tile's DMAs have landed
             barrier();
-        }
-        int j = 0;
-        for (; j + 3 <= n_tiles; j += 3) {
-            tile_step(gc, B0{}, j);
-            tile_step(gc, B1{}, j + 1);
-            tile_step(gc, B2{}, j + 2);
-        }
-        if (j < n_tiles) {
-            tile_step(gc, B0{}, j);
-            if (++j < n_tiles) tile_step(gc, B1{}, j);
-        }
-        // Group 1 is one phase behind: its last barrier ended V(n-1); group 0
-        // takes the matching barrier after its last P V.  The DMAs of tiles
-        // past the end (zeros) are drained before the workgroup can end.
-        const int lb = (n_tiles + 2) % 3;       // buffer of tile n-1 (tile -1 when n = 0)
-        if (lb == 0) last_pv(B0{});
-        else if (lb == 1) last_pv(B1{});
-        else last_pv(B2{});
-        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
-        if constexpr (GRP == 0) barrier();
-    };
-    if constexpr (!PP_OFFSET) run(std::integral_constant<int, 2>{});
-    else if (grp == 0) run(std::integral_constant<int, 0>{});
-    else run(std::integral_constant<int, 1>{});
+        };
 
-    const int qi = q0w + n;
-    const int64_t lrow = (int64_t)bh * Sq + qi;
-    const int64_t orow = out_heads ? ((int64_t)(bh / H) * Sq + qi) * out_heads + out_h0 + bh % H : lrow;
-    store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse,
-                                 vmax ? vmax + (int64_t)bkv * D : nullptr);
+        // Last P V: O += V_{n-1}^T P_{n-1}^T, V_{n-1} in buffer (n-1) mod 3; its
+        // first fragments were loaded at the end of V(n-1) (with the unused K
+        // fragments of a tile past the end).
+        auto last_pv = [&](auto bv) __attribute__((always_inline)) {
+    #pragma unroll
+            for (int i = 0; i < NSTEP; ++i) {
+                int kb, u, db;
+                pv_idx(i, kb, u, db);
+                const f16x8 vv = i < PF ? vf[i % NR] : vfrag(bv, kb, u, db);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, p[kb][u], o[db], 0, 0, 0);
+            }
+        };
+
+        auto run = [&](auto gc) __attribute__((always_inline)) {
+            constexpr int GRP = decltype(gc)::value;
+            if constexpr (GRP == 1) {
+                // Group 1 idles for the first phase; it issues its part of the
+                // DMAs of the first phase pair (K_2, V_1) there.
+                dma_k(2, B2{});
+                dma_v(1, B1{});
+                barrier();
+            }
+            int j = 0;
+            for (; j + 3 <= n_tiles; j += 3) {
+                tile_step(gc, B0{}, j);
+                tile_step(gc, B1{}, j + 1);
+                tile_step(gc, B2{}, j + 2);
+            }
+            if (j < n_tiles) {
+                tile_step(gc, B0{}, j);
+                if (++j < n_tiles) tile_step(gc, B1{}, j);
+            }
+            // Group 1 is one phase behind: its last barrier ended V(n-1); group 0
+            // takes the matching barrier after its last P V.  The DMAs of tiles
+            // past the end (zeros) are drained before the workgroup can end.
+            const int lb = (n_tiles + 2) % 3;       // buffer of tile n-1 (tile -1 when n = 0)
+            if (lb == 0) last_pv(B0{});
+            else if (lb == 1) last_pv(B1{});
+            else last_pv(B2{});
+            __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
+            if constexpr (GRP == 0) barrier();
+        };
+        if constexpr (!PP_OFFSET) run(std::integral_constant<int, 2>{});
+        else if (grp == 0) run(std::integral_constant<int, 0>{});
+        else run(std::integral_constant<int, 1>{});
+
+        const int qi = q0w + n;
+        const int64_t lrow = (int64_t)bh * Sq + qi;
+        const int64_t orow = out_heads ? ((int64_t)(bh / H) * Sq + qi) * out_heads + out_h0 + bh % H : lrow;
+        const unsigned* vmax_h = vmax ? vmax + (int64_t)bkv * D : nullptr;
+        if (slot < 0) {
+            store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse, vmax_h);
+            return;
+        }
+        // Partial piece: its rows (O / l in fp32, LSE) go to the slot with
+        // coherent stores; once every wave's stores have completed the piece
+        // is counted, and the workgroup that completes the tile folds the
+        // pieces into out (reading them with coherent loads).
+        const int r = wave * QPW + n;
+        sk_store_partial<D>(o, m_run, l_run, slot * (W * QPW) + r, qi >= Sq_b, hh, sk, vmax_h);
+        __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's slot stores are done
+        __syncthreads();
+        if (tid == 0) sk_arrived = atomicAdd(sk.cnt + tl, 1);
+        __syncthreads();
+        const int64_t x0 = (int64_t)tl * sk.nkt;
+        const int u0 = sk_unit(x0, sk), u1 = sk_unit(x0 + sk.nkt - 1, sk);
+        if (sk_arrived == u1 - u0)
+            sk_finish<D, OUT_F32, MERGE>(sk, tl, u0, u1, r, hh, orow, lrow, qi < Sq, out, lse);
+    };
+
+    if constexpr (!SK) {
+        piece(xcd_remap(blockIdx.x, gridDim.x, nxcd) + tile0, 0, -1, -1, -1);
+    } else {
+        // Share u: its iterations, cut at query tile boundaries.
+        const int u = xcd_remap(blockIdx.x, gridDim.x, nxcd);
+        int64_t it = sk_start(u, sk);
+        const int64_t it_end = sk_start(u + 1, sk);
+        for (bool first = true; it < it_end; first = false) {
+            const int tl = (int)(it / sk.nkt);
+            const int kt0 = (int)(it - (int64_t)tl * sk.nkt);
+            const int kt1 = (int)min((int64_t)sk.nkt, kt0 + (it_end - it));
+            if (!first) __syncthreads();     // every wave is done with the previous piece's LDS
+            const bool whole = kt0 == 0 && kt1 == sk.nkt;
+            piece(tile0 + tl, kt0, kt1, whole ? -1 : sk_slot(u, tl, sk), tl);
+            it += kt1 - kt0;
+        }
+    }
 }
+
+// Compute units and XCDs of the device a stream runs on, looked up once per
+// device.
+struct DevShape {
+    int cus, xcds;
+};
+constexpr int kMaxDev = 64;
+std::atomic<int> g_dev_cus[kMaxDev], g_dev_xcds[kMaxDev];
+
+DevShape dev_shape(hipStream_t stream) {
+    int dev = -1;
+    if (stream) {
+        hipDevice_t d = -1;
+        if (hipStreamGetDevice(stream, &d) == hipSuccess) dev = (int)d;
+    }
+    if (dev < 0 && hipGetDevice(&dev) != hipSuccess) dev = -1;
+    if (dev >= 0 && dev < kMaxDev) {
+        const int c = g_dev_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return {c, g_dev_xcds[dev].load(std::memory_order_relaxed)};
+    }
+    int cus = 0, xcds = 0;
+    if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    if (dev < 0 || hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1)
+        xcds = 1;
+    (void)hipGetLastError();
+    if (dev >= 0 && dev < kMaxDev) {
+        g_dev_xcds[dev].store(xcds, std::memory_order_relaxed);
+        g_dev_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    return {cus, xcds};
+}
+
+}  // namespace
+
+// Launch form of an attention call.  Full attention over the workspace:
+//  * when the last round of 8-wave workgroups (one per CU) is partly filled
+//    and a split-launch region is given, the split launch spreads that
+//    round's key tiles evenly over up to SK_MAX_UNITS workgroups (at least
+//    SK_MIN_ITERS key tiles each); it is taken when its estimated length
+//    (its share plus the launch's fixed cost, in key tiles: the second
+//    launch, the pipeline fill of its pieces and the fold of the partial
+//    rows) beats the form below;
+//  * otherwise, when that last round is at most half full, its tiles run as
+//    twice as many 4-wave workgroups of 128 query rows in a second launch.
+//    Each CU then holds at most one of them, and a lone 4-wave workgroup
+//    runs faster than an 8-wave one.  The per-row arithmetic is the same.
+// Causal grids, whose tiles differ in cost, use 4-wave workgroups throughout
+// when the grid is small.  Without a workspace: one launch of 8-wave
+// workgroups.
+Plan make_plan(int64_t BH, int Sq, int Skv, bool causal, bool ws, bool sk_region, bool varlen, int cus) {
+    Plan p{};
+    const int nq8 = (Sq + WAVES * QPW - 1) / (WAVES * QPW);
+    const int64_t blk8 = (int64_t)nq8 * BH;
+    const int64_t tail8 = blk8 % cus;
+    const int64_t nkt = (Skv + BN - 1) / BN;
+    p.form = FORM_ONE;
+    if (!ws) return p;
+    if (causal) {
+        if (blk8 < (int64_t)SMALL_GRID_ROUNDS * cus && tail8 > 0 && 2 * tail8 <= cus) p.form = FORM_ALL4;
+        return p;
+    }
+    if (sk_region && !varlen && tail8 > 0 && tail8 <= SK_MAX_UNITS) {
+        const int64_t iters = tail8 * nkt;
+        const int64_t units = std::min<int64_t>(std::min(cus, SK_MAX_UNITS), iters / SK_MIN_ITERS);
+        const int64_t sk_len = units > 0 ? (iters + units - 1) / units + SK_LAUNCH_COST : INT64_MAX;
+        const int64_t round_len = 2 * tail8 <= cus ? nkt * 11 / 20 : nkt;
+        if (units > tail8 && sk_len < round_len) {
+            p.form = FORM_SPLIT;
+            p.sk_iters = iters;
+            p.sk_units = (int)units;
+            return p;
+        }
+    }
+    if (tail8 > 0 && 2 * tail8 <= cus) p.form = FORM_HALVES;
+    return p;
+}
+
+int plan_attn(int64_t BH, int Sq, int Skv, bool causal, bool ws, bool sk_region, bool varlen, hipStream_t stream) {
+    return make_plan(BH, Sq, Skv, causal, ws, sk_region, varlen, dev_shape(stream).cus).form;
+}
+
+namespace {
 
 template <int D, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* out, float* lse,
                   int BH, int H, int G, int Sq, int Skv, float c, unsigned qsign, bool causal, const void* vws,
-                  const QNormRope* qn, const int* lq, const int* lkv, int out_heads, int out_h0, bool merge,
-                  hipStream_t stream) {
+                  void* sk_ws, const QNormRope* qn, const int* lq, const int* lkv, int out_heads, int out_h0,
+                  bool merge, hipStream_t stream) {
     const QNormRope qz{};
+    const DevShape dv = dev_shape(stream);
+    const int cus = dv.cus;
     // The workspace holds the V images, then the largest |v| per (K/V head, d).
     const unsigned* vmax =
         vws ? (const unsigned*)((const char*)vws + v_images_bytes(BH / G, Skv, D)) : nullptr;
     // One launch of workgroups of w waves over tiles [tile0, tile0 + ntile)
     // of n_qtiles per head; with halves, every tile of 2*w*QPW rows goes to
-    // two workgroups.
+    // two workgroups; with a split, sk.units workgroups share the key tiles
+    // of those query tiles.
     auto go = [&](auto kern, const QNormRope& qa, int w, int n_qtiles, int64_t tile0, int64_t ntile,
-                  bool halves) -> hipError_t {
-        const int64_t nblk = halves ? 2 * ntile : ntile;
+                  bool halves, const SplitK& sk) -> hipError_t {
+        const int64_t nblk = sk.units ? sk.units : halves ? 2 * ntile : ntile;
         if (nblk > 0x7FFFFFFF || tile0 + ntile > 0x7FFFFFFF) return hipErrorInvalidValue;
         if (nblk == 0) return hipSuccess;
         hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(w * 64), 0, stream, (const uint16_t*)q,
                            (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)vws, vmax, kv_bh_stride, out,
                            lse, Sq,
                            Skv, c, qsign, causal ? 1 : 0, n_qtiles, H, G, qa, lq, lkv, out_heads, out_h0,
-                           (int)tile0, halves ? 1 : 0);
+                           (int)tile0, halves ? 1 : 0, dv.xcds, sk);
         return hipGetLastError();
     };
+    const SplitK none{};
     const int nq8 = (Sq + WAVES * QPW - 1) / (WAVES * QPW);
     const int64_t blk8 = (int64_t)nq8 * BH;
-    const int64_t tail8 = blk8 % 256, full8 = blk8 - tail8;
-    // Workspace path: when the last round of 8-wave workgroups over 256 CUs
-    // is at most half full, those tiles run as twice as many 4-wave
-    // workgroups of 128 query rows in a second launch.  Each CU then holds at
-    // most one of them, and a lone 4-wave workgroup runs faster than an
-    // 8-wave one.  The per-row arithmetic is the same.  Causal grids, whose
-    // tiles differ in cost, use 4-wave workgroups throughout when the grid
-    // is small.
-    const bool tail_split = vws != nullptr && !causal && tail8 > 0 && tail8 <= 128;
-    const bool all4 = vws != nullptr && causal && blk8 < (int64_t)SMALL_GRID_ROUNDS * 256 && tail8 > 0 && tail8 <= 128;
+    const int64_t tail8 = blk8 % cus, full8 = blk8 - tail8;
+    const Plan pl = make_plan(BH, Sq, Skv, causal, vws != nullptr, sk_ws != nullptr, lq != nullptr, cus);
+    SplitK sk{};
+    if (pl.form == FORM_SPLIT) {
+        char* base = (char*)sk_ws;
+        sk.cnt = (int*)base;
+        sk.part_l = (float*)(base + SK_CNT_BYTES);
+        sk.part_o = (float*)(base + SK_CNT_BYTES + (int64_t)2 * SK_MAX_UNITS * WAVES * QPW * 4);
+        sk.iters = pl.sk_iters;
+        sk.units = pl.sk_units;
+        sk.nkt = (Skv + BN - 1) / BN;
+    }
+    const bool all4 = pl.form == FORM_ALL4, tail_split = pl.form == FORM_HALVES;
     // Full attention over the workspace runs its 8-wave workgroups in the
     // ping-pong form (same bits).
-    auto run = [&](auto k8, auto k4, auto kpp, const QNormRope& qa) -> hipError_t {
+    auto run = [&](auto k8, auto k4, auto kpp, auto ksk, const QNormRope& qa) -> hipError_t {
         if (all4) return go(k4, qa, 4, (Sq + 4 * QPW - 1) / (4 * QPW), 0, (int64_t)((Sq + 4 * QPW - 1) / (4 * QPW)) * BH,
-                            false);
-        if (!tail_split) return causal ? go(k8, qa, WAVES, nq8, 0, blk8, false) : go(kpp, qa, WAVES, nq8, 0, blk8, false);
-        const hipError_t e = go(kpp, qa, WAVES, nq8, 0, full8, false);
+                            false, none);
+        if (pl.form == FORM_SPLIT) {
+            const hipError_t e = go(kpp, qa, WAVES, nq8, 0, full8, false, none);
+            if (e != hipSuccess) return e;
+            return go(ksk, qa, WAVES, nq8, full8, tail8, false, sk);
+        }
+        if (!tail_split)
+            return causal ? go(k8, qa, WAVES, nq8, 0, blk8, false, none) : go(kpp, qa, WAVES, nq8, 0, blk8, false, none);
+        const hipError_t e = go(kpp, qa, WAVES, nq8, 0, full8, false, none);
         if (e != hipSuccess) return e;
-        return go(k4, qa, 4, nq8, full8, tail8, true);
+        return go(k4, qa, 4, nq8, full8, tail8, true, none);
     };
     if (merge)
         return run(attn_fwd_kernel<D, OUT_F32, false, true, true>, attn_fwd_kernel<D, OUT_F32, false, true, true, 4>,
-                   attn_pp_kernel<D, OUT_F32, false, true>, qz);
+                   attn_pp_kernel<D, OUT_F32, false, true>, attn_pp_kernel<D, OUT_F32, false, true, true>, qz);
     if (vws && qn)
         return run(attn_fwd_kernel<D, OUT_F32, true, true>, attn_fwd_kernel<D, OUT_F32, true, true, false, 4>,
-                   attn_pp_kernel<D, OUT_F32, true, false>, *qn);
+                   attn_pp_kernel<D, OUT_F32, true, false>, attn_pp_kernel<D, OUT_F32, true, false, true>, *qn);
     if (vws)
         return run(attn_fwd_kernel<D, OUT_F32, false, true>, attn_fwd_kernel<D, OUT_F32, false, true, false, 4>,
-                   attn_pp_kernel<D, OUT_F32, false, false>, qz);
-    return go(attn_fwd_kernel<D, OUT_F32, false, false>, qz, WAVES, nq8, 0, blk8, false);
+                   attn_pp_kernel<D, OUT_F32, false, false>, attn_pp_kernel<D, OUT_F32, false, false, true>, qz);
+    return go(attn_fwd_kernel<D, OUT_F32, false, false>, qz, WAVES, nq8, 0, blk8, false, none);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
-                           bool causal, bool out_f32, const void* vws, const QNormRope* qn, const int* lq,
-                           const int* lkv, int out_heads, int out_h0, bool merge, hipStream_t stream) {
+                           bool causal, bool out_f32, const void* vws, void* sk_ws, const QNormRope* qn,
+                           const int* lq, const int* lkv, int out_heads, int out_h0, bool merge,
+                           hipStream_t stream) {
     // Positive multiplier for exp2; the sign of the scale goes into Q.  A
     // zero (or vanishing) scale keeps a tiny positive multiplier so that
     // masked logits (-inf) still map to probability 0; the logits it yields
@@ -995,10 +1291,10 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t 
     if (!(c >= 1e-30f)) c = 1e-30f;
     const unsigned qsign = scale < 0.f ? 0x80008000u : 0u;
     if (D == 128)
-        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, merge, stream)
-                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, merge, stream);
-    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, merge, stream)
-                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, qn, lq, lkv, out_heads, out_h0, merge, stream);
+        return out_f32 ? launch<128, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, sk_ws, qn, lq, lkv, out_heads, out_h0, merge, stream)
+                       : launch<128, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, sk_ws, qn, lq, lkv, out_heads, out_h0, merge, stream);
+    return out_f32 ? launch<64, true>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, sk_ws, qn, lq, lkv, out_heads, out_h0, merge, stream)
+                   : launch<64, false>(q, k, v, kv_bh_stride, out, lse, BH, H, G, Sq, Skv, c, qsign, causal, vws, sk_ws, qn, lq, lkv, out_heads, out_h0, merge, stream);
 }
 
 }  // namespace dit

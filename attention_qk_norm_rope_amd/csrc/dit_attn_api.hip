@@ -131,6 +131,15 @@ int check_attn(const void* q, const void* k, const void* v, int64_t kv_bh_stride
     return DIT_OK;
 }
 
+// Bytes of prepared V (images and column maxima) for B*Hkv K/V heads; -1 for
+// sizes the kernels cannot address.
+int64_t v_part_bytes(int B, int Hkv, int Skv, int D) {
+    if (B < 1 || Hkv < 1 || Skv < 1 || (D != 64 && D != 128)) return -1;
+    const int64_t BH = (int64_t)B * Hkv;
+    if (BH > 0x7FFFFFFF || (int64_t)(Skv + 512) * D * 2 > 0x7FFFFFFF) return -1;
+    return dit::v_prep_bytes(BH, Skv, D);
+}
+
 // Attention launch shared by the entry points: optional workspace (V images),
 // optional fused Q prologue (workspace path only), Hkv K/V heads.
 int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
@@ -141,11 +150,17 @@ int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_strid
     const int st = check_attn(q, k, v, kv_bh_stride, out, lse, B, H, Hkv, Sq, Skv, D, scale, out_dtype, &r,
                               out_heads, out_h0);
     if (st != DIT_OK) return st;
+    // The workspace holds the prepared V (required), then the split-launch
+    // region (used when the workspace is large enough for it).
+    int64_t ws_used = 0;
+    bool split = false;
     if (workspace) {
         if (!aligned(workspace, 16)) return DIT_ERR_ALIGN;
-        const int64_t need = attn_fwd_workspace_bytes(B, Hkv, Skv, D);
+        const int64_t need = v_part_bytes(B, Hkv, Skv, D);
         if (need < 0 || workspace_bytes < need) return DIT_ERR_SHAPE;
-        const Range rw = range_of(workspace, need);
+        split = workspace_bytes - need >= dit::sk_bytes(D);
+        ws_used = split ? need + dit::sk_bytes(D) : need;
+        const Range rw = range_of(workspace, ws_used);
         if (overlap(rw, r.q) || overlap(rw, r.k) || overlap(rw, r.v) || overlap(rw, r.out) ||
             (lse && overlap(rw, r.lse)))
             return DIT_ERR_ALIAS;
@@ -164,17 +179,19 @@ int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_strid
         const Range rl[2] = {range_of(lq, (int64_t)B * 4), range_of(lkv, (int64_t)B * 4)};
         for (const Range& t : rl)
             if (overlap(t, r.out) || (lse && overlap(t, r.lse)) ||
-                (workspace && overlap(t, range_of(workspace, attn_fwd_workspace_bytes(B, Hkv, Skv, D)))))
+                (workspace && overlap(t, range_of(workspace, ws_used))))
                 return DIT_ERR_ALIAS;
     }
     (void)hipGetLastError();
     if (workspace) {
-        const hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * Hkv, Skv, D, lkv, Hkv, stream);
+        const hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * Hkv, Skv, D, lkv, Hkv,
+                                                split ? dit::SK_MAX_UNITS : 0, stream);
         if (e != hipSuccess) return DIT_ERR_HIP;
     }
+    void* sk_ws = split ? (char*)workspace + v_part_bytes(B, Hkv, Skv, D) : nullptr;
     return hip_status(dit::launch_attn_fwd(q, k, v, kv_bh_stride, out, lse, B * H, H, H / Hkv, Sq, Skv, D, scale,
-                                           causal != 0, out_dtype == DIT_FP32, workspace, qn, lq, lkv, out_heads,
-                                           out_h0, merge, stream));
+                                           causal != 0, out_dtype == DIT_FP32, workspace, sk_ws, qn, lq, lkv,
+                                           out_heads, out_h0, merge, stream));
 }
 
 // Shared checks of the layout entry points: a is the BSND tensor, b the BNSD slice.
@@ -202,10 +219,23 @@ int attn_fwd_kv_strided(const void* q, const void* k, const void* v, int64_t kv_
 }
 
 int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D) {
-    if (B < 1 || H < 1 || Skv < 1 || (D != 64 && D != 128)) return -1;
+    const int64_t v_part = v_part_bytes(B, H, Skv, D);
+    return v_part < 0 ? -1 : v_part + dit::sk_bytes(D);
+}
+
+int attn_fwd_launch_form(int B, int H, int Hkv, int Sq, int Skv, int D, int causal, int varlen,
+                         int64_t workspace_bytes, hipStream_t stream, int* form) {
+    if (!form) return DIT_ERR_NULL;
+    if (B < 1 || H < 1 || Sq < 1 || Skv < 1 || Hkv < 1 || Hkv > H || H % Hkv != 0) return DIT_ERR_SHAPE;
+    if (D != 64 && D != 128) return DIT_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
-    if (BH > 0x7FFFFFFF || (int64_t)(Skv + 512) * D * 2 > 0x7FFFFFFF) return -1;
-    return dit::v_prep_bytes(BH, Skv, D);
+    if (BH > 0x7FFFFFFF || BH * Sq * D > kMaxElems || workspace_bytes < 0) return DIT_ERR_SHAPE;
+    const int64_t need = v_part_bytes(B, Hkv, Skv, D);
+    if (need < 0 || (workspace_bytes > 0 && workspace_bytes < need)) return DIT_ERR_SHAPE;
+    const bool ws = workspace_bytes > 0;
+    const bool split = ws && workspace_bytes - need >= dit::sk_bytes(D);
+    *form = dit::plan_attn(BH, Sq, Skv, causal != 0, ws, split, varlen != 0, stream);
+    return DIT_OK;
 }
 
 int attn_fwd_ws(const void* q, const void* k, const void* v, int64_t kv_bh_stride, void* workspace,
@@ -390,10 +420,10 @@ int attn_fwd_noalloc(const void* q, const void* k, const void* v, int64_t kv_bh_
         const char* vg = (const char*)v + h0 * kv_bh_stride * 2;
         char* og = (char*)out + h0 * Sq * D * esize;
         float* lg = lse ? lse + h0 * Sq : nullptr;
-        hipError_t e = dit::launch_v_prep(vg, kv_bh_stride, ws, n, Skv, D, nullptr, n, stream);
+        hipError_t e = dit::launch_v_prep(vg, kv_bh_stride, ws, n, Skv, D, nullptr, n, 0, stream);
         if (e != hipSuccess) return DIT_ERR_HIP;
         e = dit::launch_attn_fwd(qg, kg, vg, kv_bh_stride, og, lg, n, n, 1, Sq, Skv, D, scale, causal != 0,
-                                 out_dtype == DIT_FP32, ws, nullptr, nullptr, nullptr, 0, 0, false, stream);
+                                 out_dtype == DIT_FP32, ws, nullptr, nullptr, nullptr, nullptr, 0, 0, false, stream);
         if (e != hipSuccess) return DIT_ERR_HIP;
     }
     return DIT_OK;

@@ -147,21 +147,30 @@ v_prep_kernel(const uint16_t* __restrict__ v, int64_t kv_bh_stride, uint16_t* __
     }
 }
 
-constexpr int COLMAX_KEYS = 1024;   // keys per block of the column pass
+// Keys per block of the column pass: about 2048 blocks in all (at least 64
+// keys, at most 1024 per block), so that small grids still fill the chip.
+int colmax_keys(int BH, int Skv, int D) {
+    const int rows = 256 / (D / 8);              // key rows one pass of a block covers
+    int64_t c = ((int64_t)Skv * BH + 2047) / 2048;
+    c = c < 64 ? 64 : c > 1024 ? 1024 : c;
+    return (int)((c + rows - 1) / rows * rows);
+}
 
 template <int D>
 hipError_t launch(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, const int* lkv, int Hkv,
-                  hipStream_t stream) {
+                  int zero_after, hipStream_t stream) {
     const int n_tiles = (Skv + BN - 1) / BN;
     const unsigned gy = (unsigned)(BH < 65535 ? BH : 65535);
     unsigned* vmax = (unsigned*)((char*)ws + v_images_bytes(BH, Skv, D));
-    const int64_t n_max = (int64_t)BH * D;
+    // The maxima start at zero (and so do the zero_after words behind them).
+    const int64_t n_max = (int64_t)BH * D + zero_after;
     hipLaunchKernelGGL(vmax_zero_kernel, dim3((unsigned)((n_max + 255) / 256)), dim3(256), 0, stream, vmax,
                        (int)n_max);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((v_colmax_kernel<D>), dim3((unsigned)((Skv + COLMAX_KEYS - 1) / COLMAX_KEYS), gy), dim3(256),
-                       0, stream, (const uint16_t*)v, kv_bh_stride, vmax, BH, Skv, COLMAX_KEYS, lkv, Hkv);
+    const int ck = colmax_keys(BH, Skv, D);
+    hipLaunchKernelGGL((v_colmax_kernel<D>), dim3((unsigned)((Skv + ck - 1) / ck), gy), dim3(256),
+                       0, stream, (const uint16_t*)v, kv_bh_stride, vmax, BH, Skv, ck, lkv, Hkv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((v_prep_kernel<D>), dim3((unsigned)n_tiles, gy), dim3(256), 0, stream,
@@ -182,9 +191,9 @@ int64_t v_prep_bytes(int64_t BH, int Skv, int D) {
 }
 
 hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D, const int* lkv,
-                         int Hkv, hipStream_t stream) {
-    if (D == 128) return launch<128>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, stream);
-    return launch<64>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, stream);
+                         int Hkv, int zero_after, hipStream_t stream) {
+    if (D == 128) return launch<128>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, zero_after, stream);
+    return launch<64>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, zero_after, stream);
 }
 
 }  // namespace dit

@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--ring-streams", type=int, default=1, choices=[1, 2],
                     help="wan workload: run the local and remote attention calls on one stream in order (1) "
                          "or concurrently on two streams (2)")
+    ap.add_argument("--no-split", action="store_true",
+                    help="give the attention calls a workspace of the V part only, which rules out the split "
+                         "launch of a partly filled last round (for comparison)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain device copies of a known size (the reference for rocprofv3's "
                          "FETCH_SIZE/WRITE_SIZE counters) and print their byte counts")
@@ -90,6 +93,18 @@ def parse():
     # The merging epilogue has no fused-Q variant: --fuse-q keeps the separate merge.
     args.fuse_merge = not (args.separate_merge or args.fuse_q)
     return args
+
+
+NO_SPLIT = False
+
+
+def ws_bytes(B: int, H: int, Skv: int, D: int) -> int:
+    """Workspace bytes of an attention call: the library's full size, or the
+    V part alone (no split launch) under --no-split."""
+    from attention_qk_norm_rope_amd import attn_fwd_workspace_bytes
+    if NO_SPLIT:
+        return B * H * (-(-Skv // 64) * 64 * D * 2 + D * 4)
+    return attn_fwd_workspace_bytes(B, H, Skv, D)
 
 
 def calibrate_copy():
@@ -164,7 +179,7 @@ def bench_ulysses(args):
     q = bsnd_to_bnsd(x, 0, hs)
     k = bsnd_to_bnsd(x, hs, hs)
     v = bsnd_to_bnsd(x, 2 * hs, hs)
-    ws = torch.empty((attn_fwd_workspace_bytes(B, hs, S, D),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((ws_bytes(B, hs, S, D),), dtype=torch.uint8, device=dev)
     ob = torch.empty((B, hs, S, D), dtype=torch.bfloat16, device=dev)
 
     def two_pass():
@@ -328,9 +343,12 @@ def run_configs(args, dev, wan) -> dict:
     import torch
 
     import oracle
-    from attention_qk_norm_rope_amd import (attn_fwd_workspace_bytes, attn_fwd_ws, attn_fwd_ws_merge, inputs,
+    from attention_qk_norm_rope_amd import (attn_fwd_launch_form, attn_fwd_ws, attn_fwd_ws_merge, inputs,
                                             qk_norm_rope_out)
     res = {}
+
+    def form(B_, H_, Sq_, Skv_, D_, w):
+        return attn_fwd_launch_form(B_, H_, Sq_, Skv_, D_, workspace_bytes=w.numel())
     bits = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
 
     # Wan2.2 Q x4: the normalised q times 4 (exact in bf16) through the same
@@ -352,7 +370,8 @@ def run_configs(args, dev, wan) -> dict:
     log("[bench] configs: wan q x4")
     (t_att,) = _time_calls(wan_q4, 2, 5, 1)
     r = _attn_entry("attn_fwd_ws + attn_fwd_ws_merge (local 1/4 + remote 3/4 of the keys)", t_att, cfg.flops(),
-                    {"workload": "Wan2.2 B1 H40 S75600 D128, normalised q x4 (logit std ~4)"})
+                    {"workload": "Wan2.2 B1 H40 S75600 D128, normalised q x4 (logit std ~4)",
+                     "launch_forms": {"local": form(B, H, S, c, D, ws), "remote": form(B, H, S, S - c, D, ws)}})
     if not args.no_cpu_baseline:
         rows = inputs.sample_rows(cfg.index, B, H, S, per_head=64)
         ref_o, ref_l = oracle.attn(bits(q4), bits(k), wan["v_bits"], cfg.scale, False, rows=rows)
@@ -382,7 +401,8 @@ def run_configs(args, dev, wan) -> dict:
     log("[bench] configs: sp share")
     (t_att,) = _time_calls(sp_step, 2, 10, 1)
     r = _attn_entry("attn_fwd_ws + 3 x attn_fwd_ws_merge (4 KV chunks of 18900 keys, fp32 accumulator)", t_att,
-                    sp.flops(), {"workload": "Wan2.2 4-way SP share: Sq 18900 x Skv 75600, H40 D128"})
+                    sp.flops(), {"workload": "Wan2.2 4-way SP share: Sq 18900 x Skv 75600, H40 D128",
+                                 "launch_forms": {"chunk": form(B, H, sp.Sq, cs, D, ws)}})
     if not args.no_cpu_baseline:
         rows = inputs.sample_rows(sp.index, B, H, sp.Sq, per_head=64)
         qs_bits = np.ascontiguousarray(wan["q0_bits"][:, :, :sp.Sq])
@@ -402,7 +422,7 @@ def run_configs(args, dev, wan) -> dict:
         qc, kc = torch.empty_like(q0c), torch.empty_like(k0c)
         w_q, w_k = torch.from_numpy(x["w_q"]).to(dev), torch.from_numpy(x["w_k"]).to(dev)
         cos_d, sin_d = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
-        wsc = torch.empty((attn_fwd_workspace_bytes(cf.B, cf.H, cf.Skv, cf.D),), dtype=torch.uint8, device=dev)
+        wsc = torch.empty((ws_bytes(cf.B, cf.H, cf.Skv, cf.D),), dtype=torch.uint8, device=dev)
         oc = torch.empty((cf.B, cf.H, cf.Sq, cf.D), dtype=torch.bfloat16, device=dev)
         lc = torch.empty((cf.B, cf.H, cf.Sq), dtype=torch.float32, device=dev)
 
@@ -417,6 +437,7 @@ def run_configs(args, dev, wan) -> dict:
         pro_bytes = 2 * (2 + 2) * cf.B * cf.H * cf.S * cf.D + 2 * cf.S * cf.D * 4
         r = _attn_entry("attn_fwd_ws", t_att, cf.flops(),
                         {"workload": f"{cf.name}: RMSNorm + RoPE prologue, attention over all keys",
+                         "launch_forms": {"all keys": form(cf.B, cf.H, cf.Sq, cf.Skv, cf.D, wsc)},
                          "prologue": _bw_entry(t_pro, pro_bytes)})
         if not args.no_cpu_baseline:
             rows = inputs.sample_rows(cf.index, cf.B, cf.H, cf.Sq, per_head=64)
@@ -530,7 +551,10 @@ def main():
     import numpy as np
     import torch
 
-    from attention_qk_norm_rope_amd import (attn_fwd_ring_overlap, attn_fwd_workspace_bytes, attn_fwd_ws,
+    global NO_SPLIT
+    NO_SPLIT = args.no_split
+    from attention_qk_norm_rope_amd import (attn_fwd_launch_form, attn_fwd_ring_overlap, attn_fwd_workspace_bytes,
+                                            attn_fwd_ws,
                                             attn_fwd_ws_fused_q, attn_fwd_ws_merge, attn_merge, inputs,
                                             qk_norm_rope, qk_norm_rope_out)
     from attention_qk_norm_rope_amd import binding
@@ -564,7 +588,7 @@ def main():
     kernels = {}
     # One workspace, sized for the largest KV window of the step.
     ws_keys = {"wan": S - S // 4, "qwen": Skv, "cosmos": Skv, "sp": Skv // max(cfg.chunks, 1)}[wl]
-    ws = torch.empty((attn_fwd_workspace_bytes(B, H, ws_keys, D),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((ws_bytes(B, H, ws_keys, D),), dtype=torch.uint8, device=dev)
     w_q = w_k = cos_d = sin_d = cos = sin = None
     if wl in ("wan", "qwen", "cosmos"):
         cos, sin = inputs.config_rope_tables(cfg)
@@ -581,7 +605,7 @@ def main():
         out_b = torch.empty_like(out_a)
         lse_a = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
         lse_b = torch.empty_like(lse_a)
-        ws_local = torch.empty((attn_fwd_workspace_bytes(B, H, c, D),), dtype=torch.uint8, device=dev)
+        ws_local = torch.empty((ws_bytes(B, H, c, D),), dtype=torch.uint8, device=dev)
         side = torch.cuda.Stream(device=dev)
         names = ["qk_norm_rope", "attn_fwd+attn_merge"]
 
@@ -719,12 +743,14 @@ def main():
     attn_flops = cfg.flops()
     if "attn_fwd" in per_kernel:
         n_attn = launches["attn_fwd"]
-        entry = ("attn_fwd_ws (per call: v_prep_kernel, then attn_fwd_kernel; a last round that would fill at "
-                 "most half the CUs runs as a second dispatch of 4-wave workgroups)")
+        entry = ("attn_fwd_ws (per call: the V rewrite kernels, then the attention launches of the form in "
+                 "launch_forms: full rounds of 8-wave workgroups, and a partly filled last round as a split "
+                 "launch over its key tiles or as 4-wave halves)")
         if wl in ("wan", "sp") and args.fuse_merge:
-            entry = ("attn_fwd_ws + attn_fwd_ws_merge (per call: v_prep_kernel, then attn_fwd_kernel; a last round "
-                     "that would fill at most half the CUs runs as a second dispatch of 4-wave workgroups; the "
-                     "second call merges into the first's output in its epilogue)")
+            entry = ("attn_fwd_ws + attn_fwd_ws_merge (per call: the V rewrite kernels, then the attention "
+                     "launches of the form in launch_forms: full rounds of 8-wave workgroups, and a partly filled "
+                     "last round as a split launch over its key tiles or as 4-wave halves; the second call merges "
+                     "into the first's output in its epilogue)")
         attn_list = per_kernel["attn_fwd"]
     else:
         # Two streams: the interval spans both overlapped calls and the merge.
@@ -741,6 +767,10 @@ def main():
                            "tflops_median": round(attn_flops / (ast["median"] * 1e-3) / 1e12, 2),
                            "tflops_best": round(attn_flops / (ast["min"] * 1e-3) / 1e12, 2),
                            "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}
+    kv_calls = {"wan": {"local": S // 4, "remote": S - S // 4}, "sp": {"chunk": Skv // max(cfg.chunks, 1)}}.get(
+        wl, {"all keys": Skv})
+    kernels["attn_fwd"]["launch_forms"] = {
+        nm: attn_fwd_launch_form(B, H, Sq, n, D, workspace_bytes=ws.numel()) for nm, n in kv_calls.items()}
     if "qk_norm_rope" in per_kernel:
         pro_bytes = (1 if args.fuse_q else 2) * (2 + 2) * B * H * S * D + 2 * S * D * 4
         kernels["qk_norm_rope"] = _bw_entry(per_kernel["qk_norm_rope"], pro_bytes)

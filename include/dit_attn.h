@@ -154,29 +154,64 @@ int attn_fwd_kv_strided(const void *q, const void *k, const void *v, int64_t kv_
  * workspace that lets the kernel stream V without converting it: first
  * launches write each 64-key tile of V once as an fp16, transposed tile image
  * into `workspace`, and the attention launch copies those images straight
- * into LDS.  Faster than attn_fwd on the same inputs; for |v| <= 65504 the
- * results are the same arithmetic (identical bits).  Any bf16 v is taken:
+ * into LDS.  Faster than attn_fwd on the same inputs.  Any bf16 v is taken:
  * a column (head, d) whose largest |v| is 2^16 or more is scaled by an exact
  * power of two 2^-e into fp16 range before the conversion, and the output's
  * component d is multiplied back by 2^e (values far below the column's
  * largest then keep an absolute accuracy of 2^(e-25)).
  *
- *   workspace        device buffer of at least attn_fwd_workspace_bytes(B, H,
- *                    Skv, D) bytes, 16-byte aligned, overlapping no other
+ *   workspace        device buffer, 16-byte aligned, overlapping no other
  *                    argument.  Its contents are scratch: overwritten by
  *                    every call, meaningless afterwards.  Calls that share a
  *                    workspace must be ordered on one stream.
- *   workspace_bytes  its size (DIT_ERR_SHAPE when too small)
+ *   workspace_bytes  its size: at least the V part, B*H * (ceil(Skv/64) * 64
+ *                    * D * 2 + D * 4) bytes (DIT_ERR_SHAPE when smaller).
+ *                    With attn_fwd_workspace_bytes(B, H, Skv, D) bytes (the
+ *                    V part plus a split region of fixed size) full
+ *                    attention may take the split launch, see below.
+ *
+ * Launch forms (attn_fwd_launch_form tells which one a call takes).  Query
+ * tiles of 256 rows run one per CU.  When the last round of tiles is partly
+ * filled:
+ *   - with the split region, and when it is estimated to be faster, the key
+ *     tiles of that round's query tiles are dealt in equal shares to one
+ *     workgroup per CU; a query tile cut between shares is assembled from
+ *     its pieces' normalised rows and LSEs with the arithmetic of
+ *     attn_merge, in key order, by the workgroup that completes it.  The
+ *     rows of those tiles then differ from attn_fwd's in rounding only;
+ *   - otherwise, when that round is at most half full, it runs as 4-wave
+ *     workgroups of 128 rows (same arithmetic).
+ * Without the split launch, and for |v| <= 65504, the results are the bits
+ * of attn_fwd.
  */
 int attn_fwd_ws(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
                 void *workspace, int64_t workspace_bytes, void *out, float *lse,
                 int B, int H, int Sq, int Skv, int D, float scale, int causal,
                 int out_dtype, hipStream_t stream);
 
-/* Workspace bytes attn_fwd_ws needs (B*H * (ceil(Skv/64) * 64 * D * 2 + D * 4):
- * the V tile images and the largest |v| of every (head, d)), or -1 for
- * arguments attn_fwd_ws would reject. */
+/* Workspace bytes for every launch form of attn_fwd_ws: the V part
+ * B*H * (ceil(Skv/64) * 64 * D * 2 + D * 4) (the V tile images and the largest
+ * |v| of every (head, d)) plus the split region, 1024 + 512 * 256 * (D + 1) * 4
+ * bytes (arrival counters, the LSEs and fp32 rows of up to 512 partial
+ * pieces of 256 query rows).  -1 for arguments attn_fwd_ws would reject. */
 int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D);
+
+/* Launch form codes of attn_fwd_launch_form. */
+enum {
+    DIT_FORM_ONE = 0,     /* one launch of 8-wave workgroups */
+    DIT_FORM_HALVES = 1,  /* full rounds, then the last round as 4-wave halves */
+    DIT_FORM_SPLIT = 2,   /* full rounds, then the split launch */
+    DIT_FORM_ALL4 = 3     /* 4-wave workgroups throughout (small causal grids) */
+};
+
+/* The launch form an attention call with these sizes takes on the device of
+ * `stream` (or the current device for the null stream): workspace_bytes = 0
+ * for a call without a workspace, Hkv K/V heads, varlen != 0 for
+ * attn_fwd_varlen.  Writes a DIT_FORM_* code to *form.  Errors: DIT_ERR_NULL
+ * (form), DIT_ERR_SHAPE (sizes an attention call would reject, or a
+ * workspace smaller than the V part). */
+int attn_fwd_launch_form(int B, int H, int Hkv, int Sq, int Skv, int D, int causal, int varlen,
+                         int64_t workspace_bytes, hipStream_t stream, int *form);
 
 /*
  * Grouped-query attention: [WAN] npu_fused_infer_attention_score takes a
@@ -192,8 +227,9 @@ int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D);
  *   - non-NULL: runs the path of attn_fwd_ws. It needs at least
  *     attn_fwd_workspace_bytes(B, Hkv, Skv, D) bytes; V is rewritten once per
  *     K/V head.
- * Both paths give identical bits. Other arguments, results and errors are as
- * for attn_fwd_ws. DIT_ERR_SHAPE when Hkv < 1 or H % Hkv != 0.
+ * Both paths give identical bits unless the split launch runs (see
+ * attn_fwd_ws). Other arguments, results and errors are as for attn_fwd_ws.
+ * DIT_ERR_SHAPE when Hkv < 1 or H % Hkv != 0.
  */
 int attn_fwd_gqa(const void *q, const void *k, const void *v, int64_t kv_bh_stride,
                  void *workspace, int64_t workspace_bytes, void *out, float *lse,
@@ -338,7 +374,8 @@ int bnsd_to_bsnd(const void *o, void *x, int B, int S, int H, int h0, int Hs, in
  * the library (each GPU the library runs on holds its own copy from the first
  * call until the process ends).  The call allocates nothing.
  *
- * Arguments, layouts and results are those of attn_fwd_ws (same bits).  The
+ * Arguments, layouts and results are those of attn_fwd_ws (the bits of
+ * attn_fwd_ws with a workspace of the V part only: no split launch).  The
  * heads are processed in groups whose V images fit in the buffer, one group
  * after another on `stream`.  Limit: one head's share, ceil(Skv/64) * 64 *
  * D * 2 + D * 4 bytes (Skv <= 262080 at D = 128, 524224 at D = 64), must

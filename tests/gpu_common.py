@@ -53,19 +53,23 @@ def workload(name: str) -> dict:
 
 
 def launch_edge_rows(B: int, H: int, Sq: int, cus: int = 256) -> list:
-    """Flat query rows at the edges of the workspace path's launch forms: the
-    first row of the first tile that the grid's mostly empty last round hands
-    to a second dispatch of 4-wave workgroups (and the first row of that
-    tile's second half), plus the rows either side of those edges."""
+    """Flat query rows of the tiles that the workspace path's second dispatch
+    takes when the last round of 256-row tiles is partly filled (4-wave
+    halves or the split launch): the rows either side of the first such
+    tile's start and middle, the first and last row of every such tile, and
+    every 17th row of the first and the last of them."""
     bm = 256
     nq = (Sq + bm - 1) // bm
     blk = nq * B * H
     tail = blk % cus
-    rows = []
-    if 0 < tail <= cus // 2:
-        t = blk - tail
+    rows = set()
+    for t in range(blk - tail, blk):
         bh, qt = divmod(t, nq)
-        for r in (qt * bm - 1, qt * bm, qt * bm + bm // 2 - 1, qt * bm + bm // 2):
-            if 0 <= r < Sq:
-                rows.append(bh * Sq + r)
-    return rows
+        lo, hi = qt * bm, min(Sq, qt * bm + bm)
+        picks = [lo, hi - 1]
+        if t == blk - tail:
+            picks += [lo - 1, lo + bm // 2 - 1, lo + bm // 2]
+        if t in (blk - tail, blk - 1):
+            picks += list(range(lo, hi, 17))
+        rows.update(bh * Sq + r for r in picks if 0 <= r < Sq)
+    return sorted(rows)

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from oracle import compare
-from attention_qk_norm_rope_amd import attn_fwd, attn_fwd_ws, attn_fwd_workspace_bytes, inputs
+from attention_qk_norm_rope_amd import attn_fwd, attn_fwd_launch_form, attn_fwd_ws, attn_fwd_workspace_bytes, inputs
 from attention_qk_norm_rope_amd.binding import DitAttnError
 from gpu_common import DEV, dev_bits, host_f64, say
 from test_gpu_attn import CASES, _ids
@@ -71,10 +71,14 @@ def test_ws_large_logits_d64():
 
 
 def test_ws_rejects_small_or_misplaced_workspace():
+    """The V part is the minimum; the full size adds the split region, and
+    anything in between runs without the split launch."""
     B, H, S, D = 1, 2, 256, 128
     q = dev_bits(inputs.random_bits(91, (B, H, S, D)))
     n = attn_fwd_workspace_bytes(B, H, S, D)
-    small = torch.empty((n - 16,), dtype=torch.uint8, device=DEV)
+    v_part = B * H * ((S // 64) * 64 * D * 2 + D * 4)
+    np.testing.assert_equal(n, v_part + 256 * 4 + 512 * 256 * (D + 1) * 4)
+    small = torch.empty((v_part - 16,), dtype=torch.uint8, device=DEV)
     with pytest.raises(DitAttnError) as e:
         attn_fwd_ws(q, q, q, small)
     assert e.value.status == 2
@@ -82,7 +86,10 @@ def test_ws_rejects_small_or_misplaced_workspace():
         out = torch.empty((n // 2,), dtype=torch.bfloat16, device=DEV)
         attn_fwd_ws(q, q, q, out, out=out[: B * H * S * D].view(B, H, S, D))
     assert e.value.status == 5
-    np.testing.assert_equal(n, B * H * ((S // 64) * 64 * D * 2 + D * 4))
+    o1, l1 = attn_fwd_ws(q, q, q, torch.empty((n - 16,), dtype=torch.uint8, device=DEV))
+    o2, l2 = attn_fwd_ws(q, q, q, torch.empty((v_part,), dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 @pytest.mark.parametrize("lo,hi", [(-20.0, 100.0), (60.0, 127.0), (15.0, 16.5)])
@@ -139,19 +146,22 @@ def test_value_range_of_v():
     assert float(np.max(np.abs(host_f64(l1) - ref_l))) <= 1e-3
 
 
-@pytest.mark.parametrize("B,H,Sq,causal", [
-    (1, 129, 256, False),     # 129 tiles of 256 rows: last round more than half full, one 8-wave launch
-    (1, 128, 256, True),      # causal, small grid, last round half full: 4-wave workgroups throughout
-    (3, 43, 300, False),      # 258 tiles = one full round + 2: 8-wave launch, then the 2 tiles as 4 halves
-    (1, 96, 256, False),      # 96 tiles, no full round: the halves launch alone
-    (2, 100, 200, False),     # 200 tiles: one 8-wave launch
+@pytest.mark.parametrize("B,H,Sq,causal,form", [
+    (1, 129, 256, False, "one"),     # 129 tiles of 256 rows: last round more than half full, one 8-wave launch
+    (1, 128, 256, True, "all4"),     # causal, small grid, last round half full: 4-wave workgroups throughout
+    (3, 43, 300, False, "halves"),   # 258 tiles = one full round + 2: 8-wave launch, then the 2 tiles as 4 halves
+    (1, 96, 256, False, "halves"),   # 96 tiles, no full round: the halves launch alone
+    (2, 100, 200, False, "one"),     # 200 tiles: one 8-wave launch
 ])
-def test_ws_workgroup_sizes_match_plain(B, H, Sq, causal):
+def test_ws_workgroup_sizes_match_plain(B, H, Sq, causal, form):
     """The workspace path launches 8-wave workgroups, 4-wave workgroups, or
     8-wave workgroups followed by the last round's tiles as 4-wave halves,
     depending on the grid; every form gives the bits of the path without a
     workspace (one 8-wave launch) and agrees with the oracle on sampled rows."""
     Skv, D = 150, 128
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        # 3 key tiles: a split launch never pays, whatever the workspace.
+        assert attn_fwd_launch_form(B, H, Sq, Skv, D, causal, attn_fwd_workspace_bytes(B, H, Skv, D)) == form
     q = inputs.random_bits(B * H + Sq, (B, H, Sq, D))
     k = inputs.random_bits(B * H + Sq + 1, (B, H, Skv, D))
     v = inputs.random_bits(B * H + Sq + 2, (B, H, Skv, D))

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from oracle import compare
-from attention_qk_norm_rope_amd import attn_fwd, attn_fwd_workspace_bytes, attn_fwd_ws
+from attention_qk_norm_rope_amd import attn_fwd, attn_fwd_launch_form, attn_fwd_workspace_bytes, attn_fwd_ws
 from attention_qk_norm_rope_amd.binding import DitAttnError
 from gpu_common import DEV, host_f64, say
 
@@ -37,19 +37,33 @@ def test_longest_key_slab():
     scale = 1 / math.sqrt(D)
     say(f"[limits] Skv = {S_MAX}: attn_fwd")
     o0, l0 = attn_fwd(q, k, v, scale=scale, out_dtype=torch.float32)
-    say(f"[limits] Skv = {S_MAX}: attn_fwd_ws")
-    ws = torch.empty((attn_fwd_workspace_bytes(1, 1, S_MAX, D),), dtype=torch.uint8, device=DEV)
+    # A workspace of the V part only: the bits of attn_fwd.
+    say(f"[limits] Skv = {S_MAX}: attn_fwd_ws, V part only")
+    v_part = (S_MAX + 63) // 64 * 64 * D * 2 + D * 4
+    ws = torch.empty((v_part,), dtype=torch.uint8, device=DEV)
     o1, l1 = attn_fwd_ws(q, k, v, ws, scale=scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    del ws, o1, l1
+    # The full workspace: the two query tiles' 131072 key tiles are split
+    # between one workgroup per CU.
+    n = attn_fwd_workspace_bytes(1, 1, S_MAX, D)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert attn_fwd_launch_form(1, 1, Sq, S_MAX, D, workspace_bytes=n) == "split"
+    say(f"[limits] Skv = {S_MAX}: attn_fwd_ws, split launch")
+    ws = torch.empty((n,), dtype=torch.uint8, device=DEV)
+    o2, l2 = attn_fwd_ws(q, k, v, ws, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
     del ws
     rows = np.array([0, 1, 127, 128, 255, 256, 299], dtype=np.int64)
     say(f"[limits] oracle on {rows.size} rows x {S_MAX} keys")
     ref_o, ref_l = oracle.attn(_bits(q), _bits(k), _bits(v), scale, False, rows=rows)
-    rep = compare.attn_report(host_f64(o0.reshape(-1, D)[torch.from_numpy(rows).to(DEV)]), ref_o,
-                              host_f64(l0.reshape(-1)[torch.from_numpy(rows).to(DEV)]), ref_l, bf16=False)
-    say(f"[limits] {rep}")
-    compare.assert_ok(rep, "longest key slab")
+    idx = torch.from_numpy(rows).to(DEV)
+    for name, o, l in (("attn_fwd", o0, l0), ("split", o2, l2)):
+        rep = compare.attn_report(host_f64(o.reshape(-1, D)[idx]), ref_o, host_f64(l.reshape(-1)[idx]), ref_l,
+                                  bf16=False)
+        say(f"[limits] {name}: {rep}")
+        compare.assert_ok(rep, f"longest key slab, {name}")
     # One key more no longer fits the kernels' 32-bit offsets.
     k2 = torch.empty((1, 1, S_MAX + 1, D), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(DitAttnError):

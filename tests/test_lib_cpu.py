@@ -55,6 +55,7 @@ def lib():
     lib.bsnd_to_bnsd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.bnsd_to_bsnd.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p]
     lib.attn_fwd_noalloc.argtypes = [p, p, p, i64, p, p, i32, i32, i32, i32, i32, f32, i32, i32, p]
+    lib.attn_fwd_launch_form.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i64, p, ctypes.POINTER(i32)]
     lib.dit_attn_status_string.restype = ctypes.c_char_p
     lib.dit_attn_version.restype = ctypes.c_char_p
     return lib
@@ -63,7 +64,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert set(names) == {"qk_norm_rope", "qk_norm_rope_out", "attn_fwd", "attn_fwd_kv_strided", "attn_fwd_ws",
-                          "attn_fwd_workspace_bytes", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_fwd_noalloc", "attn_merge", "bsnd_to_bnsd",
+                          "attn_fwd_workspace_bytes", "attn_fwd_launch_form", "attn_fwd_gqa", "attn_fwd_ws_fused_q", "attn_fwd_ws_bsnd", "attn_fwd_ws_merge", "attn_fwd_varlen", "attn_fwd_noalloc", "attn_merge", "bsnd_to_bnsd",
                           "bnsd_to_bsnd", "dit_attn_status_string",
                           "dit_attn_version"}, names
     for name in names:
@@ -130,14 +131,20 @@ def test_attn_fwd_kv_strided_rejections(lib):
     assert f(Q, K, V, (O - K) // 2, O, L, 1, 2, 256, 256, 64, 0.125, 0, BF16, None) == ALIAS
 
 
+def split_region(D):
+    """Bytes of the split-launch region: 256 arrival counters, then the LSE
+    and fp32 rows of 512 partial pieces of 256 query rows."""
+    return 256 * 4 + 512 * 256 * (D + 1) * 4
+
+
 def test_attn_fwd_workspace_bytes(lib):
     f = lib.attn_fwd_workspace_bytes
     # One fp16 image of 64 keys x D per started 64-key tile and head, then
-    # one 4-byte column maximum per (head, d).
-    assert f(1, 2, 256, 64) == 2 * 4 * 64 * 64 * 2 + 2 * 64 * 4
-    assert f(1, 1, 1, 128) == 64 * 128 * 2 + 128 * 4
-    assert f(2, 3, 65, 128) == 6 * 2 * 64 * 128 * 2 + 6 * 128 * 4
-    assert f(1, 40, 75600, 128) == 40 * 1182 * 64 * 128 * 2 + 40 * 128 * 4
+    # one 4-byte column maximum per (head, d), then the split region.
+    assert f(1, 2, 256, 64) == 2 * 4 * 64 * 64 * 2 + 2 * 64 * 4 + split_region(64)
+    assert f(1, 1, 1, 128) == 64 * 128 * 2 + 128 * 4 + split_region(128)
+    assert f(2, 3, 65, 128) == 6 * 2 * 64 * 128 * 2 + 6 * 128 * 4 + split_region(128)
+    assert f(1, 40, 75600, 128) == 40 * 1182 * 64 * 128 * 2 + 40 * 128 * 4 + split_region(128)
     assert f(0, 2, 256, 64) == -1
     assert f(1, 2, 0, 64) == -1
     assert f(1, 2, 256, 96) == -1
@@ -159,6 +166,9 @@ def test_attn_fwd_ws_rejections(lib):
     assert call(nbytes=0) == SHAPE
     assert call(ws=Q + 4096) == ALIAS                    # workspace inside q
     assert call(ws=O - need + 16) == ALIAS               # workspace runs into out
+    # With room for the split region, the region is checked against out too.
+    full = need + split_region(64)
+    assert call(ws=O - full + 16, nbytes=full) == ALIAS
     assert call(ws=L) == ALIAS                           # workspace on lse
     assert call(o=None) == NULL                          # the attention checks come first
     assert call(stride=255 * 64) == SHAPE
@@ -328,3 +338,22 @@ def test_attn_fwd_varlen_rejections(lib):
     assert call(lk=O) == ALIAS                           # lengths on the output
     assert call(Hkv=3) == SHAPE
     assert call(o=None) == NULL
+
+
+def test_attn_fwd_launch_form_rejections(lib):
+    f = lib.attn_fwd_launch_form
+    form = ctypes.c_int(-1)
+    D = 128
+    need = 4 * (64 * D * 2 + D * 4)                      # B1 H4, one 64-key tile
+
+    def call(B=1, H=4, Hkv=4, Sq=256, Skv=64, D=D, nbytes=0, out=True):
+        return f(B, H, Hkv, Sq, Skv, D, 0, 0, nbytes, None, ctypes.byref(form) if out else None)
+
+    assert call(out=False) == NULL
+    assert call(Sq=0) == SHAPE
+    assert call(Skv=0) == SHAPE
+    assert call(Hkv=3) == SHAPE
+    assert call(D=96) == UNSUP
+    assert call(nbytes=-1) == SHAPE
+    assert call(nbytes=need - 1) == SHAPE                # smaller than the V part
+    assert form.value == -1                              # untouched by a rejected call

@@ -1,7 +1,8 @@
 """attn_fwd_noalloc through the C ABI: the entry point for callers that
 cannot allocate (its V images live in the library's static scratch buffer).
 It must give the bits of attn_fwd_ws (the entry point with a caller
-workspace) and agree with the fp64 oracle, on consecutive calls that reuse
+workspace) given a workspace of the V part only (so that neither takes the
+split launch) and agree with the fp64 oracle, on consecutive calls that reuse
 the buffer -- the second with a smaller input -- and when the heads do not
 all fit in the buffer at once."""
 import ctypes
@@ -42,7 +43,9 @@ def _case(seed, B, H, Sq, Skv, D, causal, out_dtype, check_oracle=True):
     lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device=DEV)
     say(f"[noalloc] B{B} H{H} Sq{Sq} Skv{Skv} D{D} causal={causal} {out_dtype}")
     assert _noalloc(dq, dk, dv, out, lse, scale, causal) == 0
-    ws = torch.empty((attn_fwd_workspace_bytes(B, H, Skv, D),), dtype=torch.uint8, device=DEV)
+    v_part = B * H * (-(-Skv // 64) * 64 * D * 2 + D * 4)
+    assert v_part < attn_fwd_workspace_bytes(B, H, Skv, D)
+    ws = torch.empty((v_part,), dtype=torch.uint8, device=DEV)
     ro, rl = attn_fwd_ws(dq, dk, dv, ws, scale=scale, causal=causal, out_dtype=out_dtype)
     torch.cuda.synchronize()
     assert torch.equal(out, ro) and torch.equal(lse, rl), "attn_fwd_noalloc differs from attn_fwd_ws"
