@@ -39,10 +39,11 @@ layout_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int 
         const int b = (int)(bs / S);
         const int64_t bsnd = (((int64_t)b * S + s) * H + h0 + h) * D + 8 * c;
         const int64_t bnsd = (((int64_t)b * Hs + h) * S + s) * D + 8 * c;
+        // Each chunk is read and written once: non-temporal accesses.
         if constexpr (TO_BNSD)
-            *(u32x4*)(dst + bnsd) = *(const u32x4*)(src + bsnd);
+            __builtin_nontemporal_store(__builtin_nontemporal_load((const u32x4*)(src + bsnd)), (u32x4*)(dst + bnsd));
         else
-            *(u32x4*)(dst + bsnd) = *(const u32x4*)(src + bnsd);
+            __builtin_nontemporal_store(__builtin_nontemporal_load((const u32x4*)(src + bnsd)), (u32x4*)(dst + bsnd));
     }
 }
 
