@@ -8,14 +8,17 @@
 // head groups, per-batch valid lengths); the LSE is the statistic the Ring
 // Attention Overlap section merges with.
 //
-// One kernel, 8 waves x 32 query rows per workgroup, with two sources of V:
+// Workgroups of 8 waves x 32 query rows share each K/V tile in LDS, with
+// two sources of V:
 //  * VPREP: v_prep_kernel wrote fp16 V^T tile images into a workspace, and
 //    they are copied into LDS by the buffer->LDS DMA like K (attn_fwd_ws);
 //  * otherwise each iteration loads the V tile into registers and writes it
 //    into LDS in the same image layout (attn_fwd, no workspace).
-// The 8 waves share each K/V tile in LDS.  On the workspace path, a last
-// round of workgroups that would leave most CUs idle runs as 4-wave
-// workgroups of 128 query rows instead.
+// Two kernel forms: attn_fwd_kernel (the path without a workspace, causal
+// calls, and 4-wave workgroups for a mostly empty last round) and
+// attn_pp_kernel (full attention over the workspace: two wave groups one
+// phase apart, and the split launch that deals a partly filled last round's
+// key tiles evenly over the CUs).
 //
 // Epilogue variants: rows go to BNSD or to a head slice of a BSND tensor
 // (a runtime output layout), and MERGE folds each row into a running
@@ -59,8 +62,8 @@
 //    DMA into one buffer does not alias reads of the other and does not wait
 //    for the DMA before those reads.
 //  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin
-//    over 8 XCDs) works on a contiguous range of (b,h, q-tile): the query
-//    tiles of one head share that head's K/V through one XCD's L2.
+//    over the device's XCDs) works on a contiguous range of (b,h, q-tile):
+//    the query tiles of one head share that head's K/V through one XCD's L2.
 #include "internal.h"
 #include "merge_math.h"
 #include "norm_rope.h"
