@@ -99,7 +99,6 @@ constexpr int SK_LAUNCH_COST = 40;     // split launch: measured fixed cost, in 
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float P_SUM_FAST = 256.0f;   // 2^TAU, TAU = 8: a lane's tile sum below it bounds each of its P
 constexpr int RSRC_WORD3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
-constexpr int CPOL_SC1 = 16;           // buffer access cache policy: coherent across the device's L2s
 #ifndef DIT_PP_OFFSET
 #define DIT_PP_OFFSET 1
 #endif
@@ -172,11 +171,10 @@ __device__ __forceinline__ int xcd_remap(int wid, int nblk, int nx) {
 // `units` equal shares of consecutive (query tile, key tile) iterations, one
 // share per workgroup of a launch of its own, so every CU gets the same
 // number of key tiles.  A query tile that several shares cover leaves each
-// piece's normalised rows and LSE in a slot; the workgroup that completes the
-// tile's last piece folds the pieces in share order with the arithmetic of
+// piece's normalised rows and LSE in a slot; a fold launch after it combines
+// the pieces of each such tile in share order with the arithmetic of
 // attn_merge (merge_math.h).
 struct SplitK {
-    int* cnt;           // [tiles] pieces completed per split query tile; zero at launch
     float* part_l;      // [2 * units][256] LSE of the partial pieces
     float* part_o;      // [2 * units][256][D] their O / l in fp32
     int64_t iters;      // key tiles over all split query tiles (tiles * nkt)
@@ -304,121 +302,80 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[D / 32], float m_run
     if (lse && hh == 0) lse[lrow] = lm;
 }
 
-// Partial rows of the split launch are written and read with the cache
-// policy of agent-scope atomic stores and loads (sc1): those accesses are
-// coherent across the L2s of the device's XCDs, so a piece finished on one
-// XCD is seen by the workgroup that folds it on another without an L2-wide
-// write-back or invalidate.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc_l(const SplitK& sk) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)sk.part_l, (short)0, 2 * SK_MAX_UNITS * WAVES * QPW * 4,
-                                             RSRC_WORD3);
-}
-template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc_o(const SplitK& sk) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)sk.part_o, (short)0, 2 * SK_MAX_UNITS * WAVES * QPW * D * 4,
-                                             RSRC_WORD3);
-}
-
-// Row prow of a partial slot: O / l (with the column scales of store_row)
-// and the LSE, as store_row stores an fp32 row.
-template <int D>
-__device__ __forceinline__ void sk_store_partial(const f32x16 (&o)[D / 32], float m_run, float l_half, int prow,
-                                                 bool pad, int hh, const SplitK& sk, const unsigned* vmax) {
-    const float l = pair_sum(l_half);
-    const bool empty = pad || !(l > 0.f);
-    const float inv = empty ? 0.f : 1.0f / l;
-    const float lb = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l)) * LN2;
-    const __amdgpu_buffer_rsrc_t rl = sk_rsrc_l(sk), ro = sk_rsrc_o<D>(sk);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d = 32 * db + 8 * g + 4 * hh;
-            float sc[4] = {1.f, 1.f, 1.f, 1.f};
-            if (vmax) {
-                const u32x4 mb = *(const u32x4*)(vmax + d);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int x = (int)(mb[i] >> 23);
-                    sc[i] = __builtin_bit_cast(float, (unsigned)(127 + (x >= 143 ? x - 141 : 0)) << 23);
-                }
-            }
-            f32x4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = empty ? 0.f : (o[db][4 * g + i] * inv) * sc[i];
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (prow * D + d) * 4, 0,
-                                                   CPOL_SC1);
-        }
-    if (hh == 0) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lb), rl, prow * 4, 0, CPOL_SC1);
-}
-
-// Split launch: fold the partial pieces of split tile tl (shares u0..u1, in
-// that order) for row r of the tile and store the row as store_row would
-// (with MERGE, into the running out/lse).  Each fold is the two-way merge of
-// attn_merge with the fp32 result so far as side a and the next piece as
-// side b; the lane keeps the same d values as in store_row.
+// Fold launch of the split launch: the rows of the split query tiles whose
+// keys several shares covered (a tile that one share covered whole was
+// stored by it).  D/8 lanes per row, 8 consecutive values each.  The pieces
+// (shares u0..u1 of the tile, in that order) are combined with the two-way
+// merge of attn_merge, the fp32 result so far as side a and the next piece as
+// side b, and the row is stored as store_row stores it (with MERGE, folded
+// into the running out/lse).
 template <int D, bool OUT_F32, bool MERGE>
-__device__ __forceinline__ void sk_finish(const SplitK& sk, int tl, int u0, int u1, int r, int hh, int64_t orow,
-                                          int64_t lrow, bool valid, void* out, float* lse) {
-    constexpr int ROWS = WAVES * QPW;
-    if (!valid) return;
-    const __amdgpu_buffer_rsrc_t rl = sk_rsrc_l(sk), ro = sk_rsrc_o<D>(sk);
-    // One piece at a time: loading the next piece ahead costs registers that
-    // the split kernel's main loop then spills.
-    float acc[D / 32][16];
+__global__ void __launch_bounds__(256)
+sk_fold_kernel(SplitK sk, int tile0, int n_qtiles, int Sq, int H, void* __restrict__ out, float* __restrict__ lse,
+               int out_heads, int out_h0) {
+    constexpr int L = D / 8, RPB = 256 / L, ROWS = WAVES * QPW;
+    const int tl = blockIdx.x / (ROWS / RPB);
+    const int r = (blockIdx.x % (ROWS / RPB)) * RPB + threadIdx.x / L;
+    const int d0 = 8 * (threadIdx.x % L);
+    const int64_t x0 = (int64_t)tl * sk.nkt;
+    const int u0 = sk_unit(x0, sk), u1 = sk_unit(x0 + sk.nkt - 1, sk);
+    if (u0 == u1) return;
+    const int logical = tile0 + tl;
+    const int bh = logical / n_qtiles;
+    const int qi = (logical - bh * n_qtiles) * ROWS + r;
+    if (qi >= Sq) return;
+    float acc[8];
     float la = -INFINITY;
     for (int u = u0; u <= u1; ++u) {
-        const int prow = sk_slot(u, tl, sk) * ROWS + r;
-        const float lb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, prow * 4, 0, CPOL_SC1));
+        const int64_t prow = (int64_t)sk_slot(u, tl, sk) * ROWS + r;
+        const float lb = sk.part_l[prow];
         float wa = 0.f, wb = 0.f, lm = lb;
         if (u > u0) mg::weights(la, lb, wa, wb, lm);
+        const f32x4 a = *(const f32x4*)(sk.part_o + prow * D + d0);
+        const f32x4 b = *(const f32x4*)(sk.part_o + prow * D + d0 + 4);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    ro, (prow * D + 32 * db + 8 * g + 4 * hh) * 4, 0, CPOL_SC1));
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[db][4 * g + i] = u == u0 ? x[i] : mg::combine(wa, acc[db][4 * g + i], wb, x[i]);
-            }
+        for (int i = 0; i < 8; ++i) {
+            const float x = i < 4 ? a[i] : b[i - 4];
+            acc[i] = u == u0 ? x : mg::combine(wa, acc[i], wb, x);
+        }
         la = lm;
     }
+    const int64_t lrow = (int64_t)bh * Sq + qi;
+    const int64_t orow = out_heads ? ((int64_t)(bh / H) * Sq + qi) * out_heads + out_h0 + bh % H : lrow;
     float wa = 0.f, wb = 0.f, lm = la;
     if constexpr (MERGE) mg::weights(lse[lrow], la, wa, wb, lm);
+    if constexpr (MERGE) {
+        float x[8];
+        if constexpr (OUT_F32) {
+            const f32x4 a = *(const f32x4*)((const float*)out + orow * D + d0);
+            const f32x4 b = *(const f32x4*)((const float*)out + orow * D + d0 + 4);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d = 32 * db + 8 * g + 4 * hh;
-            float a[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = acc[db][4 * g + i];
-            if constexpr (MERGE) {
-                float x[4];
-                if constexpr (OUT_F32) {
-                    const f32x4 rd = *(const f32x4*)((const float*)out + orow * D + d);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) x[i] = rd[i];
-                } else {
-                    const u32x2 rd = *(const u32x2*)((const uint16_t*)out + orow * D + d);
-                    x[0] = __builtin_bit_cast(float, rd[0] << 16);
-                    x[1] = __builtin_bit_cast(float, rd[0] & 0xFFFF0000u);
-                    x[2] = __builtin_bit_cast(float, rd[1] << 16);
-                    x[3] = __builtin_bit_cast(float, rd[1] & 0xFFFF0000u);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = mg::combine(wa, x[i], wb, a[i]);
+            for (int i = 0; i < 4; ++i) {
+                x[i] = a[i];
+                x[i + 4] = b[i];
             }
-            if constexpr (OUT_F32) {
-                f32x4 w = {a[0], a[1], a[2], a[3]};
-                *(f32x4*)((float*)out + orow * D + d) = w;
-            } else {
-                u32x2 w = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])};
-                *(u32x2*)((uint16_t*)out + orow * D + d) = w;
+        } else {
+            const u32x4 rd = *(const u32x4*)((const uint16_t*)out + orow * D + d0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = __builtin_bit_cast(float, rd[i] << 16);
+                x[2 * i + 1] = __builtin_bit_cast(float, rd[i] & 0xFFFF0000u);
             }
         }
-    if (lse && hh == 0) lse[lrow] = lm;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = mg::combine(wa, x[i], wb, acc[i]);
+    }
+    if constexpr (OUT_F32) {
+        const f32x4 a = {acc[0], acc[1], acc[2], acc[3]}, b = {acc[4], acc[5], acc[6], acc[7]};
+        *(f32x4*)((float*)out + orow * D + d0) = a;
+        *(f32x4*)((float*)out + orow * D + d0 + 4) = b;
+    } else {
+        const u32x4 w = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]),
+                         pack_bf16(acc[6], acc[7])};
+        *(u32x4*)((uint16_t*)out + orow * D + d0) = w;
+    }
+    // Every lane of the row read lse[lrow] above (same wave, in order).
+    if (lse && d0 == 0) lse[lrow] = lm;
 }
 
 // Q fragments of query row qi (lane half hh): qf[t] holds elements
@@ -848,7 +805,6 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
         if constexpr (b == 0) return Vt0; else if constexpr (b == 1) return Vt1; else return Vt2;
     };
 
-    __shared__ int sk_arrived;
     const int tid = threadIdx.x;
     const int wave = uniform_int(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
     const int grp = wave >> 2;
@@ -856,8 +812,8 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
 
     // One piece of work: query tile `logical` against key tiles [kt0, kt1)
     // (kt1 < 0: all keys of the batch).  slot < 0: the rows go to out;
-    // otherwise to partial slot `slot` of split tile tl.
-    auto piece = [&](int logical, int kt0, int kt1, int slot, int tl) __attribute__((always_inline)) {
+    // otherwise to partial slot `slot`.
+    auto piece = [&](int logical, int kt0, int kt1, int slot) __attribute__((always_inline)) {
         const int bh = logical / n_qtiles;
         const int bkv = kv_head(bh, H, G);
         const int Sq_b = lq ? min(max(lq[bh / H], 0), Sq) : Sq;
@@ -1090,24 +1046,14 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
             store_row<D, OUT_F32, MERGE>(o, m_run, l_run, orow, lrow, qi < Sq, qi >= Sq_b, hh, out, lse, vmax_h);
             return;
         }
-        // Partial piece: its rows (O / l in fp32, LSE) go to the slot with
-        // coherent stores; once every wave's stores have completed the piece
-        // is counted, and the workgroup that completes the tile folds the
-        // pieces into out (reading them with coherent loads).
-        const int r = wave * QPW + n;
-        sk_store_partial<D>(o, m_run, l_run, slot * (W * QPW) + r, qi >= Sq_b, hh, sk, vmax_h);
-        __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's slot stores are done
-        __syncthreads();
-        if (tid == 0) sk_arrived = atomicAdd(sk.cnt + tl, 1);
-        __syncthreads();
-        const int64_t x0 = (int64_t)tl * sk.nkt;
-        const int u0 = sk_unit(x0, sk), u1 = sk_unit(x0 + sk.nkt - 1, sk);
-        if (sk_arrived == u1 - u0)
-            sk_finish<D, OUT_F32, MERGE>(sk, tl, u0, u1, r, hh, orow, lrow, qi < Sq, out, lse);
+        // Partial piece: its rows (O / l in fp32, with the column scales)
+        // and LSE go to the slot, for the fold launch.
+        const int64_t prow = (int64_t)slot * (W * QPW) + wave * QPW + n;
+        store_row<D, true, false>(o, m_run, l_run, prow, prow, true, qi >= Sq_b, hh, sk.part_o, sk.part_l, vmax_h);
     };
 
     if constexpr (!SK) {
-        piece(xcd_remap(blockIdx.x, gridDim.x, nxcd) + tile0, 0, -1, -1, -1);
+        piece(xcd_remap(blockIdx.x, gridDim.x, nxcd) + tile0, 0, -1, -1);
     } else {
         // Share u: its iterations, cut at query tile boundaries.
         const int u = xcd_remap(blockIdx.x, gridDim.x, nxcd);
@@ -1119,7 +1065,7 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
             const int kt1 = (int)min((int64_t)sk.nkt, kt0 + (it_end - it));
             if (!first) __syncthreads();     // every wave is done with the previous piece's LDS
             const bool whole = kt0 == 0 && kt1 == sk.nkt;
-            piece(tile0 + tl, kt0, kt1, whole ? -1 : sk_slot(u, tl, sk), tl);
+            piece(tile0 + tl, kt0, kt1, whole ? -1 : sk_slot(u, tl, sk));
             it += kt1 - kt0;
         }
     }
@@ -1243,9 +1189,8 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
     SplitK sk{};
     if (pl.form == FORM_SPLIT) {
         char* base = (char*)sk_ws;
-        sk.cnt = (int*)base;
-        sk.part_l = (float*)(base + SK_CNT_BYTES);
-        sk.part_o = (float*)(base + SK_CNT_BYTES + (int64_t)2 * SK_MAX_UNITS * WAVES * QPW * 4);
+        sk.part_l = (float*)base;
+        sk.part_o = (float*)(base + (int64_t)2 * SK_MAX_UNITS * WAVES * QPW * 4);
         sk.iters = pl.sk_iters;
         sk.units = pl.sk_units;
         sk.nkt = (Skv + BN - 1) / BN;
@@ -1253,13 +1198,22 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
     const bool all4 = pl.form == FORM_ALL4, tail_split = pl.form == FORM_HALVES;
     // Full attention over the workspace runs its 8-wave workgroups in the
     // ping-pong form (same bits).
-    auto run = [&](auto k8, auto k4, auto kpp, auto ksk, const QNormRope& qa) -> hipError_t {
+    // The split launch is followed by its fold launch.
+    auto fold = [&](auto kf) -> hipError_t {
+        constexpr int RPB = 256 / (D / 8);
+        hipLaunchKernelGGL(kf, dim3((unsigned)(tail8 * (WAVES * QPW / RPB))), dim3(256), 0, stream, sk, (int)full8,
+                           nq8, Sq, H, out, lse, out_heads, out_h0);
+        return hipGetLastError();
+    };
+    auto run = [&](auto k8, auto k4, auto kpp, auto ksk, auto kf, const QNormRope& qa) -> hipError_t {
         if (all4) return go(k4, qa, 4, (Sq + 4 * QPW - 1) / (4 * QPW), 0, (int64_t)((Sq + 4 * QPW - 1) / (4 * QPW)) * BH,
                             false, none);
         if (pl.form == FORM_SPLIT) {
-            const hipError_t e = go(kpp, qa, WAVES, nq8, 0, full8, false, none);
+            hipError_t e = go(kpp, qa, WAVES, nq8, 0, full8, false, none);
             if (e != hipSuccess) return e;
-            return go(ksk, qa, WAVES, nq8, full8, tail8, false, sk);
+            e = go(ksk, qa, WAVES, nq8, full8, tail8, false, sk);
+            if (e != hipSuccess) return e;
+            return fold(kf);
         }
         if (!tail_split)
             return causal ? go(k8, qa, WAVES, nq8, 0, blk8, false, none) : go(kpp, qa, WAVES, nq8, 0, blk8, false, none);
@@ -1269,13 +1223,16 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
     };
     if (merge)
         return run(attn_fwd_kernel<D, OUT_F32, false, true, true>, attn_fwd_kernel<D, OUT_F32, false, true, true, 4>,
-                   attn_pp_kernel<D, OUT_F32, false, true>, attn_pp_kernel<D, OUT_F32, false, true, true>, qz);
+                   attn_pp_kernel<D, OUT_F32, false, true>, attn_pp_kernel<D, OUT_F32, false, true, true>,
+                   sk_fold_kernel<D, OUT_F32, true>, qz);
     if (vws && qn)
         return run(attn_fwd_kernel<D, OUT_F32, true, true>, attn_fwd_kernel<D, OUT_F32, true, true, false, 4>,
-                   attn_pp_kernel<D, OUT_F32, true, false>, attn_pp_kernel<D, OUT_F32, true, false, true>, *qn);
+                   attn_pp_kernel<D, OUT_F32, true, false>, attn_pp_kernel<D, OUT_F32, true, false, true>,
+                   sk_fold_kernel<D, OUT_F32, false>, *qn);
     if (vws)
         return run(attn_fwd_kernel<D, OUT_F32, false, true>, attn_fwd_kernel<D, OUT_F32, false, true, false, 4>,
-                   attn_pp_kernel<D, OUT_F32, false, false>, attn_pp_kernel<D, OUT_F32, false, false, true>, qz);
+                   attn_pp_kernel<D, OUT_F32, false, false>, attn_pp_kernel<D, OUT_F32, false, false, true>,
+                   sk_fold_kernel<D, OUT_F32, false>, qz);
     return go(attn_fwd_kernel<D, OUT_F32, false, false>, qz, WAVES, nq8, 0, blk8, false, none);
 }
 

@@ -184,8 +184,7 @@ int attn_common(const void* q, const void* k, const void* v, int64_t kv_bh_strid
     }
     (void)hipGetLastError();
     if (workspace) {
-        const hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * Hkv, Skv, D, lkv, Hkv,
-                                                split ? dit::SK_MAX_UNITS : 0, stream);
+        const hipError_t e = dit::launch_v_prep(v, kv_bh_stride, workspace, B * Hkv, Skv, D, lkv, Hkv, stream);
         if (e != hipSuccess) return DIT_ERR_HIP;
     }
     void* sk_ws = split ? (char*)workspace + v_part_bytes(B, Hkv, Skv, D) : nullptr;
@@ -420,7 +419,7 @@ int attn_fwd_noalloc(const void* q, const void* k, const void* v, int64_t kv_bh_
         const char* vg = (const char*)v + h0 * kv_bh_stride * 2;
         char* og = (char*)out + h0 * Sq * D * esize;
         float* lg = lse ? lse + h0 * Sq : nullptr;
-        hipError_t e = dit::launch_v_prep(vg, kv_bh_stride, ws, n, Skv, D, nullptr, n, 0, stream);
+        hipError_t e = dit::launch_v_prep(vg, kv_bh_stride, ws, n, Skv, D, nullptr, n, stream);
         if (e != hipSuccess) return DIT_ERR_HIP;
         e = dit::launch_attn_fwd(qg, kg, vg, kv_bh_stride, og, lg, n, n, 1, Sq, Skv, D, scale, causal != 0,
                                  out_dtype == DIT_FP32, ws, nullptr, nullptr, nullptr, nullptr, 0, 0, false, stream);

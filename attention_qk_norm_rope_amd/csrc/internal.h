@@ -27,20 +27,19 @@ struct QNormRope {
     const float* sin_t;  // [Sq, D]
     float eps;
 };
-// sk_ws (workspace path, may be null): a region of sk_bytes(D) bytes whose
-// first SK_MAX_UNITS words are zero; full attention then runs a partly
-// filled last round of query tiles as a split launch over their key tiles.
+// sk_ws (workspace path, may be null): a region of sk_bytes(D) bytes; full
+// attention may then run a partly filled last round of query tiles as a
+// split launch over their key tiles, followed by a fold launch.
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, int64_t kv_bh_stride,
                            void* out, float* lse, int BH, int H, int G, int Sq, int Skv, int D, float scale,
                            bool causal, bool out_f32, const void* vws, void* sk_ws, const QNormRope* qn,
                            const int* lq, const int* lkv, int out_heads, int out_h0, bool merge,
                            hipStream_t stream);
 
-// Split-launch region: arrival counters, then the LSE and the fp32 O / l of
-// up to 2 * SK_MAX_UNITS partial pieces of 256 query rows.
+// Split-launch region: the LSE and the fp32 O / l of up to 2 * SK_MAX_UNITS
+// partial pieces of 256 query rows.
 constexpr int SK_MAX_UNITS = 256;
-constexpr int64_t SK_CNT_BYTES = (int64_t)SK_MAX_UNITS * 4;
-inline int64_t sk_bytes(int D) { return SK_CNT_BYTES + (int64_t)2 * SK_MAX_UNITS * 256 * (D + 1) * 4; }
+inline int64_t sk_bytes(int D) { return (int64_t)2 * SK_MAX_UNITS * 256 * (D + 1) * 4; }
 
 // Launch form of an attention call (the DIT_FORM_* codes of the header):
 // one launch of 8-wave workgroups; 8-wave rounds then the last round as
@@ -63,9 +62,8 @@ int plan_attn(int64_t BH, int Sq, int Skv, bool causal, bool ws, bool sk_region,
 int64_t v_images_bytes(int64_t BH, int Skv, int D);
 int64_t v_prep_bytes(int64_t BH, int Skv, int D);
 // With lkv != null, head bh (of B*Hkv) keeps keys < lkv[bh / Hkv] and zeros the rest.
-// The zero_after 32-bit words that follow the maxima are set to zero too.
 hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D, const int* lkv,
-                         int Hkv, int zero_after, hipStream_t stream);
+                         int Hkv, hipStream_t stream);
 
 // RMSNorm + interleaved rotary of q_src/k_src into q/k (equal pointers: in
 // place); a tensor whose source is null is skipped.

@@ -158,12 +158,11 @@ int colmax_keys(int BH, int Skv, int D) {
 
 template <int D>
 hipError_t launch(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, const int* lkv, int Hkv,
-                  int zero_after, hipStream_t stream) {
+                  hipStream_t stream) {
     const int n_tiles = (Skv + BN - 1) / BN;
     const unsigned gy = (unsigned)(BH < 65535 ? BH : 65535);
     unsigned* vmax = (unsigned*)((char*)ws + v_images_bytes(BH, Skv, D));
-    // The maxima start at zero (and so do the zero_after words behind them).
-    const int64_t n_max = (int64_t)BH * D + zero_after;
+    const int64_t n_max = (int64_t)BH * D;
     hipLaunchKernelGGL(vmax_zero_kernel, dim3((unsigned)((n_max + 255) / 256)), dim3(256), 0, stream, vmax,
                        (int)n_max);
     hipError_t e = hipGetLastError();
@@ -191,9 +190,9 @@ int64_t v_prep_bytes(int64_t BH, int Skv, int D) {
 }
 
 hipError_t launch_v_prep(const void* v, int64_t kv_bh_stride, void* ws, int BH, int Skv, int D, const int* lkv,
-                         int Hkv, int zero_after, hipStream_t stream) {
-    if (D == 128) return launch<128>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, zero_after, stream);
-    return launch<64>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, zero_after, stream);
+                         int Hkv, hipStream_t stream) {
+    if (D == 128) return launch<128>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, stream);
+    return launch<64>(v, kv_bh_stride, ws, BH, Skv, lkv, Hkv, stream);
 }
 
 }  // namespace dit

@@ -177,8 +177,8 @@ int attn_fwd_kv_strided(const void *q, const void *k, const void *v, int64_t kv_
  *     tiles of that round's query tiles are dealt in equal shares to one
  *     workgroup per CU; a query tile cut between shares is assembled from
  *     its pieces' normalised rows and LSEs with the arithmetic of
- *     attn_merge, in key order, by the workgroup that completes it.  The
- *     rows of those tiles then differ from attn_fwd's in rounding only;
+ *     attn_merge, in key order, by a fold launch that follows.  The rows of
+ *     those tiles then differ from attn_fwd's in rounding only;
  *   - otherwise, when that round is at most half full, it runs as 4-wave
  *     workgroups of 128 rows (same arithmetic).
  * Without the split launch, and for |v| <= 65504, the results are the bits
@@ -191,9 +191,9 @@ int attn_fwd_ws(const void *q, const void *k, const void *v, int64_t kv_bh_strid
 
 /* Workspace bytes for every launch form of attn_fwd_ws: the V part
  * B*H * (ceil(Skv/64) * 64 * D * 2 + D * 4) (the V tile images and the largest
- * |v| of every (head, d)) plus the split region, 1024 + 512 * 256 * (D + 1) * 4
- * bytes (arrival counters, the LSEs and fp32 rows of up to 512 partial
- * pieces of 256 query rows).  -1 for arguments attn_fwd_ws would reject. */
+ * |v| of every (head, d)) plus the split region, 512 * 256 * (D + 1) * 4
+ * bytes (the LSEs and fp32 rows of up to 512 partial pieces of 256 query
+ * rows).  -1 for arguments attn_fwd_ws would reject. */
 int64_t attn_fwd_workspace_bytes(int B, int H, int Skv, int D);
 
 /* Launch form codes of attn_fwd_launch_form. */

@@ -77,7 +77,7 @@ def test_ws_rejects_small_or_misplaced_workspace():
     q = dev_bits(inputs.random_bits(91, (B, H, S, D)))
     n = attn_fwd_workspace_bytes(B, H, S, D)
     v_part = B * H * ((S // 64) * 64 * D * 2 + D * 4)
-    np.testing.assert_equal(n, v_part + 256 * 4 + 512 * 256 * (D + 1) * 4)
+    np.testing.assert_equal(n, v_part + 512 * 256 * (D + 1) * 4)
     small = torch.empty((v_part - 16,), dtype=torch.uint8, device=DEV)
     with pytest.raises(DitAttnError) as e:
         attn_fwd_ws(q, q, q, small)

@@ -1,14 +1,15 @@
 """The split launch of the workspace path.  When the last round of 256-row
 query tiles is partly filled, the key tiles of that round's query tiles are
 dealt in equal shares to one workgroup per CU; a query tile cut between
-shares is assembled from its pieces with the merge arithmetic.
+shares is assembled from its pieces with the merge arithmetic by a fold
+launch that follows.
 
 Checked here: which launch form a call takes; every row of split tiles
 (tiles cut into several pieces, ragged key and query tails) against the
-oracle; repeatability (the pieces are folded in key order, whichever
-workgroup finishes last); rows outside the split tiles keep the bits of the
-unsplit form; and the bit relations between entry points that take the
-same form (fused Q, BSND store, merging epilogue, grouped K/V heads)."""
+oracle; repeatability (the pieces are folded in key order); rows outside
+the split tiles keep the bits of the unsplit form; and the bit relations
+between entry points that take the same form (fused Q, BSND store, merging
+epilogue, grouped K/V heads)."""
 import math
 
 import numpy as np

@@ -132,9 +132,9 @@ def test_attn_fwd_kv_strided_rejections(lib):
 
 
 def split_region(D):
-    """Bytes of the split-launch region: 256 arrival counters, then the LSE
-    and fp32 rows of 512 partial pieces of 256 query rows."""
-    return 256 * 4 + 512 * 256 * (D + 1) * 4
+    """Bytes of the split-launch region: the LSE and fp32 rows of 512 partial
+    pieces of 256 query rows."""
+    return 512 * 256 * (D + 1) * 4
 
 
 def test_attn_fwd_workspace_bytes(lib):
