@@ -50,9 +50,14 @@
 //    P is at most 2^TAU, log2 units) that P stands and the tile max is not
 //    even computed; this is the common case once a row's max is known, and
 //    such tiles skip the O rescale.  Otherwise the running max moves up to
-//    the tile max wherever that is larger and P is taken again.  O and the LSE use the sum
-//    of the fp16-rounded P that multiplied V: the applied weights sum to 1,
-//    and the sum is within 2^-11 relative of the exact one.
+//    the tile max wherever that is larger and P is taken again.  O and the
+//    LSE use the sum of the fp16-rounded P that multiplied V, so the applied
+//    weights sum to 1 (the sum is within 2^-11 relative of the exact one).
+//    It is taken with v_fma_mix_f32 (an fp16 half times 1.0 plus the fp32
+//    sum: two per packed pair).  The dot-product instructions (v_dot2*)
+//    would add a pair in one instruction, but on gfx950 they do not issue
+//    while another wave of the SIMD runs MFMAs (about 38 cycles each against
+//    8), and the softmax runs beside MFMAs.
 //  * exp is exp2 of fma(s, scale*log2(e), -m); the scale sign is folded into
 //    Q (an exact bf16 negation) so the multiplier is always positive.
 //  * LDS layouts are swizzled in 16-byte slots so that the 16 lanes that
@@ -223,13 +228,22 @@ __device__ __forceinline__ void tile_max(const f32x16 (&s)[KB], float c, float t
     m_run = grow ? m_new : m_run;
 }
 
+// acc + lo + hi of a packed fp16 pair, in fp32 (the conversions are exact):
+// v_fma_mix_f32 with a multiplier of 1.0, which the compiler does not form
+// from the equivalent C (it emits a conversion and an add per half).
+__device__ __forceinline__ float add_f16_pair(unsigned pk, float acc) {
+    float lo, hi;
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(pk), "v"(acc));
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(hi) : "v"(pk), "v"(lo));
+    return hi;
+}
+
 // P for unit (kb, u, e) = two scores: exp2(s*c - m), packed to fp16, summed.
 __device__ __forceinline__ unsigned p_pair(float s0, float s1, float c, float neg_m, float& lsum) {
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, neg_m));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, neg_m));
     const unsigned pk = pack_f16(p0, p1);
-    lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, lsum, false);
+    lsum = add_f16_pair(pk, lsum);
     return pk;
 }
 
@@ -785,6 +799,8 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
     constexpr int NSTEP = KB * DT;                    // score MFMAs per tile = P V MFMAs per tile
     static_assert(KDMA >= 1 && KDMA * W * 1024 == TILE * 2, "tile shape");
     static_assert(NSTEP == KB * 2 * DB, "pairs of one score and one P V MFMA");
+    constexpr int SP = NSTEP / (2 * KDMA);            // M-phase steps per DMA chunk issued
+    static_assert(SP > 2 && SP * 2 * KDMA == NSTEP, "DMA chunks spread over the steps of a phase");
     constexpr int PF = 2;                             // fragment prefetch distance (steps)
     constexpr int NR = PF + 1;                        // fragment registers in the ring
     // vmcnt that leaves one tile's DMAs (2*KDMA per wave) in flight.
@@ -831,30 +847,35 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
 
         const int n_tiles = q0 >= Sq_b || Skv <= 0 ? 0 : (Skv + BN - 1) / BN;
 
+        // DMA of this wave's 1 KB chunk i of K tile `tile` (keys past the
+        // piece read as zeros) or of V image tile `tile` (tiles past the
+        // image read as zeros) into buffer b.
         const uint16_t* kbh = k + (int64_t)bkv * kv_bh_stride + (int64_t)kt0 * BN * D;
-        auto dma_k = [&](int tile, auto b) {
+        auto dma_k1 = [&](int tile, auto b, int i) {
             const int kv0 = tile * BN;
             const int left = Skv - kv0;
             const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(kbh + (int64_t)kv0 * D), (short)0, left > 0 ? left * D * 2 : 0, RSRC_WORD3);
-    #pragma unroll
-            for (int i = 0; i < KDMA; ++i) {
-                const int s = (wave * KDMA + i) * 64 + lane;
-                const int key = s / SL;
-                const int slot = (s % SL) ^ kswz<D>(key);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Kbuf(b) + (wave * KDMA + i) * 512), 16,
-                                                         (key * D + 8 * slot) * 2, 0, 0, 0);
-            }
+            const int s = (wave * KDMA + i) * 64 + lane;
+            const int key = s / SL;
+            const int slot = (s % SL) ^ kswz<D>(key);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Kbuf(b) + (wave * KDMA + i) * 512), 16,
+                                                     (key * D + 8 * slot) * 2, 0, 0, 0);
         };
         const uint16_t* vbh = vws + ((int64_t)bkv * n_vt_all + kt0) * TILE;
-        auto dma_v = [&](int tile, auto b) {
-            // Tiles past the image read as zeros.
+        auto dma_v1 = [&](int tile, auto b, int i) {
             const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(vbh + (int64_t)min(tile, n_vt - 1) * TILE), (short)0, tile < n_vt ? TILE * 2 : 0, RSRC_WORD3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Vbuf(b) + (wave * KDMA + i) * 512), 16,
+                                                     ((wave * KDMA + i) * 64 + lane) * 16, 0, 0, 0);
+        };
+        auto dma_k = [&](int tile, auto b) {
     #pragma unroll
-            for (int i = 0; i < KDMA; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Vbuf(b) + (wave * KDMA + i) * 512), 16,
-                                                         ((wave * KDMA + i) * 64 + lane) * 16, 0, 0, 0);
+            for (int i = 0; i < KDMA; ++i) dma_k1(tile, b, i);
+        };
+        auto dma_v = [&](int tile, auto b) {
+    #pragma unroll
+            for (int i = 0; i < KDMA; ++i) dma_v1(tile, b, i);
         };
         auto kfrag = [&](auto b, int kb, int t) {
             const int key = 32 * kb + n;
@@ -916,6 +937,15 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
         // One tile: M(j) then V(j) of group GRP.  b = j mod 3 selects the buffers.
         // Each group runs its own copy of the loop, so the DMAs sit at fixed
         // points of each copy (the compiler then sees which are in flight).
+        //
+        // DMAs: in its M(j) each group issues its half of K_{j+2} and V_{j+1},
+        // one 1 KB chunk every SP steps: a burst of DMA issue stalls the
+        // wave behind it, and in the softmax phase that stall would be on
+        // the critical path.  Both tiles are first read by the fragment
+        // prefetch at the end of group 0's V(j+1), phase 2j+3 (group 0 runs
+        // M(j) in phase 2j, group 1 in phase 2j+1).  Group 0 waits for its
+        // half at the end of M(j+1) (phase 2j+2, leaving that phase's batch
+        // in flight); group 1 at the end of its V(j), also phase 2j+2.
         auto tile_step = [&](auto gc, auto bc, int j) __attribute__((always_inline)) {
             constexpr int GRP = decltype(gc)::value;
             constexpr int b = decltype(bc)::value;
@@ -924,7 +954,7 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
             using BN1 = std::integral_constant<int, (b + 1) % 3>;  // K_{j+1}, V_{j+1}
             using BN2 = std::integral_constant<int, (b + 2) % 3>;  // K_{j+2}
             // ---- M(j)
-            if constexpr (GRP == 0 || GRP == 2) {
+            if constexpr (GRP == 2) {
                 dma_k(j + 2, BN2{});
                 dma_v(j + 1, BN1{});
             }
@@ -942,18 +972,21 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
                 pv_idx(i, kb, u, db);
                 s[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % NR], qf[i / KB], s[i % KB], 0, 0, 0);
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % NR], p[kb][u], o[db], 0, 0, 0);
+                if constexpr (GRP != 2) {
+                    if (i % SP == 2) {
+                        const int ch = i / SP;
+                        if (ch < KDMA) dma_k1(j + 2, BN2{}, ch);
+                        else dma_v1(j + 1, BN1{}, ch - KDMA);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (PP_PRIO) __builtin_amdgcn_s_setprio(0);
-            // Group 0: its DMAs of the phase pair before have landed (one batch,
-            // issued at the start of this phase, stays in flight).
+            // Group 0: its DMAs of the phase pair before have landed (this
+            // phase's batch stays in flight).
             if constexpr (GRP == 0) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);
             if constexpr (GRP != 2) barrier();
             // ---- V(j)
-            if constexpr (GRP == 1) {
-                dma_k(j + 3, BK{});
-                dma_v(j + 2, BN2{});
-            }
             const int kv0 = j * BN;
             if (kv0 + BN > Skv) mask_tile(s, kv0, Skv, false, 0, hh);
             // Softmax of the tile (the same rule as attn_fwd_kernel, see there).
@@ -987,8 +1020,8 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
             // First fragments of M(j+1): K_{j+1}, and V_j (buffer b).
     #pragma unroll
             for (int i = 0; i < PF; ++i) load_step(BN1{}, BK{}, i);
-            if constexpr (GRP == 1) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);   // its DMAs of the pair before
-            if constexpr (GRP == 2) __builtin_amdgcn_s_waitcnt(0x0F70);           // this tile's DMAs have landed
+            // Group 1: its DMAs of M(j) have landed; one group: this tile's.
+            if constexpr (GRP != 0) __builtin_amdgcn_s_waitcnt(0x0F70);
             barrier();
         };
 
@@ -1007,13 +1040,7 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
 
         auto run = [&](auto gc) __attribute__((always_inline)) {
             constexpr int GRP = decltype(gc)::value;
-            if constexpr (GRP == 1) {
-                // Group 1 idles for the first phase; it issues its part of the
-                // DMAs of the first phase pair (K_2, V_1) there.
-                dma_k(2, B2{});
-                dma_v(1, B1{});
-                barrier();
-            }
+            if constexpr (GRP == 1) barrier();   // group 1 idles for the first phase
             int j = 0;
             for (; j + 3 <= n_tiles; j += 3) {
                 tile_step(gc, B0{}, j);
