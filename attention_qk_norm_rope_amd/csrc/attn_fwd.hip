@@ -779,9 +779,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 // the VALU busy; the roles swap at each barrier.  Per row, the operations and
 // their order are those of attn_fwd_kernel (same bits).
 // K and V tiles sit in three LDS buffers each (tile t in buffer t mod 3).
-// The DMAs of K_{j+2} and V_{j+1} are issued in the phase pair that starts
-// with group 0's M(j); each wave waits for its own part of them two phases
-// later (vmcnt), and they are read after the barrier that follows.
+// Each group issues its half of the DMAs of K_{j+2} and V_{j+1} during its
+// own M(j), spread over the MFMA steps; each wave waits for its part (vmcnt)
+// before the barrier after which they are first read (see tile_step).
 template <int D, bool OUT_F32, bool FQ, bool MERGE, bool SK = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
