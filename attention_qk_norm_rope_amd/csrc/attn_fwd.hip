@@ -782,7 +782,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 // Each group issues its half of the DMAs of K_{j+2} and V_{j+1} during its
 // own M(j), spread over the MFMA steps; each wave waits for its part (vmcnt)
 // before the barrier after which they are first read (see tile_step).
-template <int D, bool OUT_F32, bool FQ, bool MERGE, bool SK = false>
+template <int D, bool OUT_F32, bool FQ, bool MERGE, bool SK = false, bool VREG = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -794,6 +794,7 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
                SplitK sk) {
     constexpr int W = 8;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
+    static_assert(!VREG || (!FQ && !MERGE && !SK && PP_OFFSET), "V through registers: the plain call only");
     constexpr int TILE = BN * D;
     constexpr int KDMA = TILE * 2 / 1024 / W;         // 1 KB DMA chunks per wave per tile
     constexpr int NSTEP = KB * DT;                    // score MFMAs per tile = P V MFMAs per tile
@@ -806,12 +807,15 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
     // vmcnt that leaves one tile's DMAs (2*KDMA per wave) in flight.
     constexpr int WAIT_ONE_BATCH = 0x0F70 | (2 * KDMA);
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Ks2[TILE];
+    // V buffers first: their LDS offsets (below 48 KB) then fit the 16-bit
+    // immediate of ds_write, so staging V through registers needs no
+    // per-buffer address registers.
     __shared__ __attribute__((aligned(16))) uint16_t Vt0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vt1[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vt2[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks2[TILE];
     auto Kbuf = [&](auto bc) -> uint16_t* {
         constexpr int b = decltype(bc)::value % 3;
         if constexpr (b == 0) return Ks0; else if constexpr (b == 1) return Ks1; else return Ks2;
@@ -873,6 +877,37 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
     #pragma unroll
             for (int i = 0; i < KDMA; ++i) dma_k1(tile, b, i);
         };
+        // V through registers (no workspace): thread (kp, dc) loads keys 2kp,
+        // 2kp+1 at d-chunk dc (8 elements) of a V tile and writes them, as
+        // fp16 key pairs, into that tile's V^T image in LDS (the layout the
+        // workspace images have).  With D = 128 each group stages half of
+        // the d-chunks; with D = 64 group 0 stages all of them.
+        constexpr int VDC = D / 8;                    // d-chunks per key row
+        const int v_kp = lane & 31, v_dc = (wave * 64 + lane) >> 5;
+        const bool v_on = VREG && uniform_int(wave * 2) < VDC;
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(v + (int64_t)bkv * kv_bh_stride + (int64_t)kt0 * BN * D), (short)0,
+            VREG && Skv > 0 ? Skv * D * 2 : 0, RSRC_WORD3);
+        u32x4 vst[2];
+        auto load_v = [&](int tile) {
+            if (v_on) {
+    #pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    vst[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rv, (int)(((unsigned)(tile * BN + 2 * v_kp + i) * D + 8u * v_dc) * 2u), 0, 0);
+            }
+        };
+        // Row d = 8 dc + e of the image holds this thread's key pair in slot
+        // (col >> 3) ^ ((d >> 1) & 7) = sx ^ (e >> 1), sx below.  The element
+        // offset is 512 dc + 64 e + 8 slot + (col & 7): the slot's XOR touches
+        // bits 3-4 only, so one register, an XOR with 8 (e >> 1) and 64 e as
+        // the immediate address all eight rows.
+        const int v_col = vt_col(2 * v_kp);           // even: keys 2kp, 2kp+1 stay adjacent
+        const int v_sx = (v_col >> 3) ^ ((4 * v_dc) & 7);
+        int v_off = 8 * v_dc * BN + 8 * v_sx + (v_col & 7);
+        auto store_v1 = [&](auto b, int e) {
+            if (v_on) *(unsigned*)(Vbuf(b) + (v_off ^ (8 * (e >> 1))) + e * BN) = pick_pair_f16(vst[0], vst[1], e);
+        };
         auto dma_v = [&](int tile, auto b) {
     #pragma unroll
             for (int i = 0; i < KDMA; ++i) dma_v1(tile, b, i);
@@ -923,11 +958,22 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
         // mod 3 = 2), which P_{-1} = 0 multiplies in M(0).
         dma_k(0, B0{});
         dma_k(1, B1{});
-        dma_v(0, B0{});
+        if constexpr (!VREG) {
+            dma_v(0, B0{});
+        } else {
+            // V_0 into its image now; V_1's rows stay in registers for the end
+            // of M(0).
+            load_v(0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): V_0 (and K_0, K_1)
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) store_v1(B0{}, e);
+            load_v(1);
+        }
     #pragma unroll
         for (int i = 0; i < TILE / (W * 512); ++i)
             *(u32x4*)(Vt2 + (i * W * 64 + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        if constexpr (!VREG) __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0); V_1's loads stay in flight
         barrier();
 
         using B2 = std::integral_constant<int, 2>;
@@ -976,15 +1022,37 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
                     if (i % SP == 2) {
                         const int ch = i / SP;
                         if (ch < KDMA) dma_k1(j + 2, BN2{}, ch);
-                        else dma_v1(j + 1, BN1{}, ch - KDMA);
+                        else if constexpr (!VREG) dma_v1(j + 1, BN1{}, ch - KDMA);
+                    }
+                }
+                if constexpr (VREG) {
+                    // V_{j+1} (its rows loaded at the end of V(j-1)) into its
+                    // image, one or two d rows per step of the second half,
+                    // beside the MFMAs.  Only this phase's K chunks may still
+                    // be in flight.
+                    constexpr int HALF = NSTEP / 2, EPS = 8 / HALF;
+                    static_assert(EPS * HALF == 8 && 2 < HALF, "V rows spread over the second half");
+                    if (i == HALF) {
+                        __builtin_amdgcn_s_waitcnt(0x0F70 | KDMA);
+                        // Opaque here, so the buffer's row addresses are formed
+                        // per conversion instead of living across the loop
+                        // (which spilled).
+                        asm volatile("" : "+v"(v_off));
+                    }
+                    if (i >= HALF) {
+    #pragma unroll
+                        for (int t = 0; t < EPS; ++t) store_v1(BN1{}, (i - HALF) * EPS + t);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (PP_PRIO) __builtin_amdgcn_s_setprio(0);
             // Group 0: its DMAs of the phase pair before have landed (this
-            // phase's batch stays in flight).
-            if constexpr (GRP == 0) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);
+            // phase's batch stays in flight).  V through registers: the wait
+            // at the middle of the phase covered them; the image rows written
+            // in this phase land before the barrier.
+            if constexpr (GRP == 0 && !VREG) __builtin_amdgcn_s_waitcnt(WAIT_ONE_BATCH);
+            if constexpr (VREG) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
             if constexpr (GRP != 2) barrier();
             // ---- V(j)
             const int kv0 = j * BN;
@@ -1017,11 +1085,22 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
     #pragma unroll
                     for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
             }
+            // V through registers: V_{j+2}'s rows, converted in the middle of
+            // M(j+1) (loaded here, after the scores are dead, to keep them out
+            // of the softmax's registers).
+            if constexpr (VREG) load_v(j + 2);
             // First fragments of M(j+1): K_{j+1}, and V_j (buffer b).
     #pragma unroll
             for (int i = 0; i < PF; ++i) load_step(BN1{}, BK{}, i);
-            // Group 1: its DMAs of M(j) have landed; one group: this tile's.
-            if constexpr (GRP != 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+            // Group 1: its DMAs of M(j) have landed (with V through registers,
+            // V_{j+2}'s row loads, issued after them in this phase, may stay
+            // in flight); one group: this tile's.
+            if constexpr (GRP == 1 && VREG) {
+                if (v_on) __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
+                else __builtin_amdgcn_s_waitcnt(0x0F70);
+            } else if constexpr (GRP != 0) {
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+            }
             barrier();
         };
 
@@ -1260,6 +1339,9 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
         return run(attn_fwd_kernel<D, OUT_F32, false, true>, attn_fwd_kernel<D, OUT_F32, false, true, false, 4>,
                    attn_pp_kernel<D, OUT_F32, false, false>, attn_pp_kernel<D, OUT_F32, false, false, true>,
                    sk_fold_kernel<D, OUT_F32, false>, qz);
+    // Without a workspace: full attention in the ping-pong form with V staged
+    // through registers; causal calls in the interleaved form.
+    if (!causal) return go(attn_pp_kernel<D, OUT_F32, false, false, false, true>, qz, WAVES, nq8, 0, blk8, false, none);
     return go(attn_fwd_kernel<D, OUT_F32, false, false>, qz, WAVES, nq8, 0, blk8, false, none);
 }
 
