@@ -14,11 +14,11 @@
 //    they are copied into LDS by the buffer->LDS DMA like K (attn_fwd_ws);
 //  * otherwise each iteration loads the V tile into registers and writes it
 //    into LDS in the same image layout (attn_fwd, no workspace).
-// Two kernel forms: attn_fwd_kernel (the path without a workspace, causal
-// calls, and 4-wave workgroups for a mostly empty last round) and
-// attn_pp_kernel (full attention over the workspace: two wave groups one
-// phase apart, and the split launch that deals a partly filled last round's
-// key tiles evenly over the CUs).
+// Two kernel forms: attn_fwd_kernel (causal calls, and 4-wave workgroups
+// for a mostly empty last round) and attn_pp_kernel (full attention: two
+// wave groups one phase apart, V from the workspace images or staged
+// through registers, and the split launch that deals a partly filled last
+// round's key tiles evenly over the CUs).
 //
 // Epilogue variants: rows go to BNSD or to a head slice of a BSND tensor
 // (a runtime output layout), and MERGE folds each row into a running
