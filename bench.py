@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the DiT attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan|qwen|cosmos|sp|ulysses]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan|qwen|cosmos|sp|ulysses|plain]
                     [--no-cpu-baseline] [--no-configs]
 
 One step is one pass of the whole path over one batch of synthetic input.
@@ -38,6 +38,10 @@ Other workloads (--workload) are per-config measurements:
   qwen / cosmos: prologue (out of place), attn_fwd_ws over all keys;
   sp: attn_fwd_ws + 3 x attn_fwd_ws_merge over KV chunks of 18900 keys (Sq 18900);
       --separate-merge: 4 x attn_fwd_ws + 3 fp32 attn_merge.
+  ulysses: the head-slice layout kernels of one rank of a 4-way Ulysses split, and
+      that rank's attention stored back into BSND two ways.
+  plain: attn_fwd without a workspace against attn_fwd_ws at the Wan2.2 local
+      window, Qwen-Image and Cosmos-Predict shapes.
 """
 from __future__ import annotations
 
@@ -66,7 +70,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="wan", choices=["wan", "qwen", "cosmos", "sp", "ulysses"],
+    ap.add_argument("--workload", default="wan", choices=["wan", "qwen", "cosmos", "sp", "ulysses", "plain"],
                     help="ulysses: only the BSND<->BNSD head-slice layout kernels of one rank of a 4-way "
                          "Ulysses split at the Wan2.2 shape (reported in GB/s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -218,6 +222,70 @@ def bench_ulysses(args):
                     "bnsd_to_bsnd": {"avg_ms": round(t_post, 4), "bytes": nbytes, "gbs": gbs(t_post),
                                      "frac_hbm_peak": round(nbytes / (t_post * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}},
         "attention_to_bsnd_ms": att, "attention_to_bsnd_same_bits": same,
+    }), flush=True)
+
+
+def bench_plain(args):
+    """attn_fwd without a workspace (V staged through registers inside the
+    attention kernel) against attn_fwd_ws (V rewritten into the workspace
+    first, V rewrite included in its time), interleaved call by call with HIP
+    events, at the Wan2.2 local window and the Qwen-Image and Cosmos-Predict
+    shapes; fp32 output.  Where both take one 8-wave launch the outputs are
+    the same bits; otherwise the workspace path's split launch differs in
+    the last bits of the split tiles' rows."""
+    import torch
+    from attention_qk_norm_rope_amd import attn_fwd, attn_fwd_launch_form, attn_fwd_workspace_bytes, attn_fwd_ws
+    dev = torch.device("cuda:0")
+    shapes = [("Wan2.2 local window", 1, 40, 75600, 18900), ("Qwen-Image", 1, 24, 4312, 4312),
+              ("Cosmos-Predict", 2, 16, 12480, 12480)]
+    D = 128
+    n_rep = max(3, args.steps)
+    res = {}
+    for name, B, H, Sq, Skv in shapes:
+        g = torch.Generator(device=dev)
+        g.manual_seed(Sq)
+        q = torch.randn((B, H, Sq, D), device=dev, generator=g).bfloat16()
+        k = torch.randn((B, H, Skv, D), device=dev, generator=g).bfloat16()
+        v = torch.randn((B, H, Skv, D), device=dev, generator=g).bfloat16()
+        ws = torch.empty((attn_fwd_workspace_bytes(B, H, Skv, D),), dtype=torch.uint8, device=dev)
+        o_pl = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+        o_ws = torch.empty_like(o_pl)
+        calls = {"attn_fwd": lambda: attn_fwd(q, k, v, out=o_pl, return_lse=False),
+                 "attn_fwd_ws": lambda: attn_fwd_ws(q, k, v, ws, out=o_ws, return_lse=False)}
+        ts = {c: [] for c in calls}
+        for _ in range(max(1, args.warmup)):
+            for fn in calls.values():
+                fn()
+        torch.cuda.synchronize()
+        for _ in range(n_rep):
+            for c, fn in calls.items():
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                ts[c].append(a.elapsed_time(b))
+        flop = 4.0 * B * H * Sq * Skv * D
+        entry = {"B": B, "H": H, "Sq": Sq, "Skv": Skv, "D": D,
+                 "ws_launch_form": attn_fwd_launch_form(B, H, Sq, Skv, D, workspace_bytes=ws.numel())}
+        for c in calls:
+            med = _stats(ts[c])["median"]
+            entry[c] = {"median_ms": round(med, 4), "tflops": round(flop / (med * 1e-3) / 1e12, 2),
+                        "frac_bf16_peak": round(flop / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        entry["same_bits"] = bool(torch.equal(o_pl, o_ws))
+        entry["max_abs_diff"] = float((o_pl - o_ws).abs().max())
+        res[name] = entry
+        log(f"[bench] plain {name}: attn_fwd {entry['attn_fwd']['frac_bf16_peak']:.4f}, "
+            f"attn_fwd_ws {entry['attn_fwd_ws']['frac_bf16_peak']:.4f}")
+    wan = res["Wan2.2 local window"]["attn_fwd"]
+    print(json.dumps({
+        "metric": "attn_fwd without a workspace, TFLOP/s (auxiliary measurement, not the headline metric)",
+        "value": wan["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": n_rep, "warmup": args.warmup,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "attn_fwd (no workspace) and attn_fwd_ws, fp32 output, at the Wan2.2 local window "
+                               "(B1 H40 Sq75600 Skv18900), Qwen-Image (B1 H24 S4312) and Cosmos-Predict "
+                               "(B2 H16 S12480), D128"},
+        "shapes": res,
     }), flush=True)
 
 
@@ -536,11 +604,11 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    if args.workload == "ulysses":
+    if args.workload in ("ulysses", "plain"):
         if args.gpus != 1:
             print("bench.py measures one GPU only.", file=sys.stderr)
             sys.exit(2)
-        bench_ulysses(args)
+        (bench_ulysses if args.workload == "ulysses" else bench_plain)(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
