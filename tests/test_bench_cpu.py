@@ -32,6 +32,14 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
+@pytest.mark.parametrize("workload", ["ulysses", "plain"])
+def test_auxiliary_workloads_refuse_more_than_one_gpu(workload):
+    r = _run("--workload", workload, "--gpus", "2", "--steps", "1", "--warmup", "0")
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
 def test_option_rules(monkeypatch):
     mod = _bench_module()
     monkeypatch.setattr(sys, "argv", ["bench.py"])
