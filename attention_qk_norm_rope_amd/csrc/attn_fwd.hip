@@ -961,8 +961,8 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
         if constexpr (!VREG) {
             dma_v(0, B0{});
         } else {
-            // V_0 into its image now; V_1's rows stay in registers for the end
-            // of M(0).
+            // V_0 into its image now; V_1's rows stay in registers for the
+            // second half of M(0).
             load_v(0);
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): V_0 (and K_0, K_1)
     #pragma unroll
@@ -984,7 +984,9 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
         // Each group runs its own copy of the loop, so the DMAs sit at fixed
         // points of each copy (the compiler then sees which are in flight).
         //
-        // DMAs: in its M(j) each group issues its half of K_{j+2} and V_{j+1},
+        // DMAs: in its M(j) each group issues its half of K_{j+2} and V_{j+1}
+        // (K only when V goes through registers; V_{j+1}'s image is then
+        // written in the second half of M(j), see there),
         // one 1 KB chunk every SP steps: a burst of DMA issue stalls the
         // wave behind it, and in the softmax phase that stall would be on
         // the critical path.  Both tiles are first read by the fragment
