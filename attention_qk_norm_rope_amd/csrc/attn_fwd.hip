@@ -8,17 +8,18 @@
 // head groups, per-batch valid lengths); the LSE is the statistic the Ring
 // Attention Overlap section merges with.
 //
-// Workgroups of 8 waves x 32 query rows share each K/V tile in LDS, with
-// two sources of V:
-//  * VPREP: v_prep_kernel wrote fp16 V^T tile images into a workspace, and
+// Workgroups of 8 (or 4) waves x 32 query rows share each K/V tile in LDS,
+// with two sources of V:
+//  * the workspace: v_prep_kernel wrote fp16 V^T tile images into it, and
 //    they are copied into LDS by the buffer->LDS DMA like K (attn_fwd_ws);
-//  * otherwise each iteration loads the V tile into registers and writes it
-//    into LDS in the same image layout (attn_fwd, no workspace).
-// Two kernel forms: attn_fwd_kernel (causal calls, and 4-wave workgroups
-// for a mostly empty last round) and attn_pp_kernel (full attention: two
-// wave groups one phase apart, V from the workspace images or staged
-// through registers, and the split launch that deals a partly filled last
-// round's key tiles evenly over the CUs).
+//  * otherwise (attn_fwd, no workspace) the ping-pong kernel loads each V
+//    tile into registers and writes it into LDS in the same image layout.
+// Two kernel forms: attn_pp_kernel (8-wave workgroups: two wave groups one
+// phase apart, V from the workspace images or staged through registers,
+// full or causal attention, and the split launch that deals a partly filled
+// last round's key tiles evenly over the CUs) and attn_fwd_kernel (4-wave
+// workgroups interleaving scores, softmax and P V within each wave: a
+// mostly empty last round, and small causal grids).
 //
 // Epilogue variants: rows go to BNSD or to a head slice of a BSND tensor
 // (a runtime output layout), and MERGE folds each row into a running
@@ -474,7 +475,7 @@ __device__ __forceinline__ void load_q(const uint16_t* qbh, int Sq, int qi, int 
 // slice of the softmax and the LDS fragment reads of the next chunk.  The
 // lazy O rescale of tile j is applied after P_{j-1} V_{j-1}.  One barrier
 // per tile; during sub-iteration j the DMAs of K_{j+2} and V_j are in flight.
-template <int D, bool OUT_F32, bool FQ, bool VPREP, bool MERGE = false, int W = WAVES>
+template <int D, bool OUT_F32, bool FQ, bool MERGE = false, int W = WAVES>
 __global__ void __attribute__((amdgpu_flat_work_group_size(W * 64, W * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -484,7 +485,6 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
                    int n_qtiles, int H, int G, QNormRope qn, const int* __restrict__ lq,
                    const int* __restrict__ lkv, int out_heads, int out_h0, int tile0, int halves, int nxcd,
                    SplitK) {
-    static_assert(W == WAVES || (W == 4 && VPREP), "4-wave workgroups read V from the workspace only");
     constexpr int BM = W * QPW;
     constexpr int DT = D / 16, DB = D / 32, KB = BN / 32, SL = D / 8;
     constexpr int TILE = BN * D;                         // elements of one K or V tile
@@ -552,33 +552,6 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
         }
     };
     // V tile `tile` of this head is the image at vbh + tile*TILE (tile < n_vt).
-    // V through registers (no workspace): thread (kp, dc) of wave w loads
-    // keys 2kp, 2kp+1 at d-chunk dc (8 elements) of tile j at the start of
-    // the iteration and writes them, as fp16 key pairs, into the V^T image
-    // layout at its end.  Lanes vary kp fastest, so one wave's stores of a
-    // given d fill a whole 128-byte image row.
-    constexpr int VDC = D / 8;                        // d-chunks per key row
-    const int v_kp = lane & 31, v_dc = (wave * 64 + lane) >> 5;
-    const bool v_on = VDC * 32 == W * 64 || v_dc < VDC;       // every thread when D = 128
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(v + (int64_t)bkv * kv_bh_stride), (short)0, VPREP ? 0 : Skv * D * 2, RSRC_WORD3);
-    u32x4 vst[2];
-    auto load_v = [&](int kv0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            vst[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((kv0 + 2 * v_kp + i) * D + 8 * v_dc) * 2, 0, 0);
-    };
-    auto store_v = [&](auto b) {
-        if (v_on) {
-            const int col = vt_col(2 * v_kp);         // even: keys 2kp, 2kp+1 stay adjacent
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = 8 * v_dc + e;
-                *(unsigned*)(Vbuf(b) + d * BN + 8 * ((col >> 3) ^ ((d >> 1) & 7)) + (col & 7)) =
-                    pick_pair_f16(vst[0], vst[1], e);
-            }
-        }
-    };
     const uint16_t* vbh = vws + (int64_t)bkv * n_vt * TILE;
     auto dma_v = [&](int tile, auto b) {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -622,7 +595,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
         const std::integral_constant<int, 1 - decltype(b)::value> nb{};
         const int kv0 = j * BN;
         dma_k(kv0 + 2 * BN, b);        // K_{j+2} -> the buffer K_j used
-        if constexpr (VPREP) dma_v(j, b);      // V_j -> the buffer V_{j-2} used
+        dma_v(j, b);      // V_j -> the buffer V_{j-2} used
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -668,11 +641,6 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
                     w4[kb][u][e] = p_pair(sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1], c, neg_m, lsum);
                 }
             }
-            // Without a workspace, V_j is loaded into registers half-way
-            // through (a short live range) and stored at the end.
-            if constexpr (!VPREP) {
-                if (t == NCH / 2) load_v(kv0);
-            }
             __builtin_amdgcn_sched_barrier(0);
         }
         // P was taken against the running max.  Unless every lane's tile sum
@@ -703,7 +671,6 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
                 for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
         }
         if (needs_mask(kv0 + BN)) mask_tile(sn, kv0 + BN, Skv, causal, q0w + n, hh);
-        if constexpr (!VPREP) store_v(b);     // V_j -> the buffer V_{j-2} used
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K_{j+2}, V_j have landed in LDS
         __syncthreads();
     };
@@ -838,7 +805,9 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
         const int bkv = kv_head(bh, H, G);
         const int Sq_b = lq ? min(max(lq[bh / H], 0), Sq) : Sq;
         const int Skv_b = lkv ? min(max(lkv[bh / H], 0), Skv_all) : Skv_all;
-        const int q0 = (logical - bh * n_qtiles) * (W * QPW);
+        // Causal: the longest query tiles of each head first.
+        const int qt = logical - bh * n_qtiles;
+        const int q0 = (causal ? n_qtiles - 1 - qt : qt) * (W * QPW);
         const int q0w = q0 + wave * QPW;
         const int kt_end = kt1 < 0 ? (Skv_b + BN - 1) / BN : kt1;
         // Keys of the piece, counted from key kt0 * BN, and its V image tiles
@@ -849,7 +818,10 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
         bf16x8 qf[DT];
         load_q<D, FQ>(q + (int64_t)bh * Sq * D, Sq, q0w + n, hh, qsign, qn, qf);
 
-        const int n_tiles = q0 >= Sq_b || Skv <= 0 ? 0 : (Skv + BN - 1) / BN;
+        // Causal: key tiles up to the workgroup's last row only (the split
+        // launch, with kt0 > 0, is never causal).
+        int n_tiles = q0 >= Sq_b || Skv <= 0 ? 0 : (Skv + BN - 1) / BN;
+        if (causal) n_tiles = min(n_tiles, (min(q0 + W * QPW, Sq_b) - 1) / BN + 1);
 
         // DMA of this wave's 1 KB chunk i of K tile `tile` (keys past the
         // piece read as zeros) or of V image tile `tile` (tiles past the
@@ -1058,7 +1030,7 @@ attn_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, c
             if constexpr (GRP != 2) barrier();
             // ---- V(j)
             const int kv0 = j * BN;
-            if (kv0 + BN > Skv) mask_tile(s, kv0, Skv, false, 0, hh);
+            if (kv0 + BN > Skv || (causal && kv0 + BN - 1 > q0w)) mask_tile(s, kv0, Skv, causal, q0w + n, hh);
             // Softmax of the tile (the same rule as attn_fwd_kernel, see there).
             float alpha = 1.0f, lsum = 0.f;
             bool grow = false;
@@ -1313,7 +1285,7 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
                            nq8, Sq, H, out, lse, out_heads, out_h0);
         return hipGetLastError();
     };
-    auto run = [&](auto k8, auto k4, auto kpp, auto ksk, auto kf, const QNormRope& qa) -> hipError_t {
+    auto run = [&](auto k4, auto kpp, auto ksk, auto kf, const QNormRope& qa) -> hipError_t {
         if (all4) return go(k4, qa, 4, (Sq + 4 * QPW - 1) / (4 * QPW), 0, (int64_t)((Sq + 4 * QPW - 1) / (4 * QPW)) * BH,
                             false, none);
         if (pl.form == FORM_SPLIT) {
@@ -1324,27 +1296,25 @@ hipError_t launch(const void* q, const void* k, const void* v, int64_t kv_bh_str
             return fold(kf);
         }
         if (!tail_split)
-            return causal ? go(k8, qa, WAVES, nq8, 0, blk8, false, none) : go(kpp, qa, WAVES, nq8, 0, blk8, false, none);
+            return go(kpp, qa, WAVES, nq8, 0, blk8, false, none);
         const hipError_t e = go(kpp, qa, WAVES, nq8, 0, full8, false, none);
         if (e != hipSuccess) return e;
         return go(k4, qa, 4, nq8, full8, tail8, true, none);
     };
     if (merge)
-        return run(attn_fwd_kernel<D, OUT_F32, false, true, true>, attn_fwd_kernel<D, OUT_F32, false, true, true, 4>,
+        return run(attn_fwd_kernel<D, OUT_F32, false, true, 4>,
                    attn_pp_kernel<D, OUT_F32, false, true>, attn_pp_kernel<D, OUT_F32, false, true, true>,
                    sk_fold_kernel<D, OUT_F32, true>, qz);
     if (vws && qn)
-        return run(attn_fwd_kernel<D, OUT_F32, true, true>, attn_fwd_kernel<D, OUT_F32, true, true, false, 4>,
+        return run(attn_fwd_kernel<D, OUT_F32, true, false, 4>,
                    attn_pp_kernel<D, OUT_F32, true, false>, attn_pp_kernel<D, OUT_F32, true, false, true>,
                    sk_fold_kernel<D, OUT_F32, false>, *qn);
     if (vws)
-        return run(attn_fwd_kernel<D, OUT_F32, false, true>, attn_fwd_kernel<D, OUT_F32, false, true, false, 4>,
+        return run(attn_fwd_kernel<D, OUT_F32, false, false, 4>,
                    attn_pp_kernel<D, OUT_F32, false, false>, attn_pp_kernel<D, OUT_F32, false, false, true>,
                    sk_fold_kernel<D, OUT_F32, false>, qz);
-    // Without a workspace: full attention in the ping-pong form with V staged
-    // through registers; causal calls in the interleaved form.
-    if (!causal) return go(attn_pp_kernel<D, OUT_F32, false, false, false, true>, qz, WAVES, nq8, 0, blk8, false, none);
-    return go(attn_fwd_kernel<D, OUT_F32, false, false>, qz, WAVES, nq8, 0, blk8, false, none);
+    // Without a workspace: the ping-pong form with V staged through registers.
+    return go(attn_pp_kernel<D, OUT_F32, false, false, false, true>, qz, WAVES, nq8, 0, blk8, false, none);
 }
 
 }  // namespace
