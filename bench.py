@@ -41,7 +41,7 @@ Other workloads (--workload) are per-config measurements:
   ulysses: the head-slice layout kernels of one rank of a 4-way Ulysses split, and
       that rank's attention stored back into BSND two ways.
   plain: attn_fwd without a workspace against attn_fwd_ws at the Wan2.2 local
-      window, Qwen-Image and Cosmos-Predict shapes.
+      window, Qwen-Image and Cosmos-Predict shapes, and a causal call.
 """
 from __future__ import annotations
 
@@ -229,19 +229,19 @@ def bench_plain(args):
     """attn_fwd without a workspace (V staged through registers inside the
     attention kernel) against attn_fwd_ws (V rewritten into the workspace
     first, V rewrite included in its time), interleaved call by call with HIP
-    events, at the Wan2.2 local window and the Qwen-Image and Cosmos-Predict
-    shapes; fp32 output.  Where both take one 8-wave launch the outputs are
+    events, at the Wan2.2 local window, the Qwen-Image and Cosmos-Predict
+    shapes and a causal call (B1 H40 S18900; half the FLOP); fp32 output.  Where both take one 8-wave launch the outputs are
     the same bits; otherwise the workspace path's split launch differs in
     the last bits of the split tiles' rows."""
     import torch
     from attention_qk_norm_rope_amd import attn_fwd, attn_fwd_launch_form, attn_fwd_workspace_bytes, attn_fwd_ws
     dev = torch.device("cuda:0")
-    shapes = [("Wan2.2 local window", 1, 40, 75600, 18900), ("Qwen-Image", 1, 24, 4312, 4312),
-              ("Cosmos-Predict", 2, 16, 12480, 12480)]
+    shapes = [("Wan2.2 local window", 1, 40, 75600, 18900, False), ("Qwen-Image", 1, 24, 4312, 4312, False),
+              ("Cosmos-Predict", 2, 16, 12480, 12480, False), ("causal, B1 H40 S18900", 1, 40, 18900, 18900, True)]
     D = 128
     n_rep = max(3, args.steps)
     res = {}
-    for name, B, H, Sq, Skv in shapes:
+    for name, B, H, Sq, Skv, causal in shapes:
         g = torch.Generator(device=dev)
         g.manual_seed(Sq)
         q = torch.randn((B, H, Sq, D), device=dev, generator=g).bfloat16()
@@ -250,8 +250,8 @@ def bench_plain(args):
         ws = torch.empty((attn_fwd_workspace_bytes(B, H, Skv, D),), dtype=torch.uint8, device=dev)
         o_pl = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
         o_ws = torch.empty_like(o_pl)
-        calls = {"attn_fwd": lambda: attn_fwd(q, k, v, out=o_pl, return_lse=False),
-                 "attn_fwd_ws": lambda: attn_fwd_ws(q, k, v, ws, out=o_ws, return_lse=False)}
+        calls = {"attn_fwd": lambda: attn_fwd(q, k, v, out=o_pl, causal=causal, return_lse=False),
+                 "attn_fwd_ws": lambda: attn_fwd_ws(q, k, v, ws, out=o_ws, causal=causal, return_lse=False)}
         ts = {c: [] for c in calls}
         for _ in range(max(1, args.warmup)):
             for fn in calls.values():
@@ -265,9 +265,9 @@ def bench_plain(args):
                 b.record()
                 torch.cuda.synchronize()
                 ts[c].append(a.elapsed_time(b))
-        flop = 4.0 * B * H * Sq * Skv * D
-        entry = {"B": B, "H": H, "Sq": Sq, "Skv": Skv, "D": D,
-                 "ws_launch_form": attn_fwd_launch_form(B, H, Sq, Skv, D, workspace_bytes=ws.numel())}
+        flop = 4.0 * B * H * Sq * Skv * D / (2 if causal else 1)
+        entry = {"B": B, "H": H, "Sq": Sq, "Skv": Skv, "D": D, "causal": causal,
+                 "ws_launch_form": attn_fwd_launch_form(B, H, Sq, Skv, D, causal, workspace_bytes=ws.numel())}
         for c in calls:
             med = _stats(ts[c])["median"]
             entry[c] = {"median_ms": round(med, 4), "tflops": round(flop / (med * 1e-3) / 1e12, 2),
@@ -283,8 +283,8 @@ def bench_plain(args):
         "value": wan["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": n_rep, "warmup": args.warmup,
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "attn_fwd (no workspace) and attn_fwd_ws, fp32 output, at the Wan2.2 local window "
-                               "(B1 H40 Sq75600 Skv18900), Qwen-Image (B1 H24 S4312) and Cosmos-Predict "
-                               "(B2 H16 S12480), D128"},
+                               "(B1 H40 Sq75600 Skv18900), Qwen-Image (B1 H24 S4312), Cosmos-Predict "
+                               "(B2 H16 S12480) and causal B1 H40 S18900, D128"},
         "shapes": res,
     }), flush=True)
 
