@@ -23,6 +23,7 @@ CASES = [
     (1, 6, 3, 257, 191, 64, True, torch.float32),
     (1, 4, 1, 129, 700, 128, False, torch.float32),     # one K/V head for all (multi-query)
     (2, 3, 3, 200, 100, 128, True, torch.bfloat16),     # Hkv = H: plain multi-head
+    (1, 10, 2, 4000, 4000, 128, True, torch.bfloat16),  # causal, 160 tiles in one 8-wave launch
 ]
 
 

@@ -21,6 +21,7 @@ CASES = [
     (3, 2, 2, 300, 333, 128, False, torch.bfloat16, [300, 17, 129], [333, 64, 200]),
     (2, 4, 2, 257, 400, 64, True, torch.float32, [257, 100], [1, 400]),
     (3, 2, 1, 128, 128, 128, False, torch.float32, [0, 128, 50], [128, 0, 65]),
+    (2, 5, 5, 4000, 4000, 128, True, torch.float32, [4000, 2500], [4000, 3100]),   # causal, one 8-wave launch
 ]
 
 

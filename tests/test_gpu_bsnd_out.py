@@ -21,6 +21,7 @@ CASES = [  # B, H, Sq, Skv, D, causal, out dtype, output heads, first head
     (1, 4, 257, 333, 128, True, torch.float32, 4, 0),
     (2, 2, 129, 64, 128, False, torch.bfloat16, 7, 5),
     (1, 1, 1, 1, 64, False, torch.float32, 3, 2),
+    (1, 10, 4000, 4000, 128, True, torch.bfloat16, 12, 1),   # causal, 160 tiles in one 8-wave launch
 ]
 
 

@@ -41,6 +41,7 @@ CASES = [  # B, H, Sq, Skv, D, causal, out dtype, grid
     (1, 3, 600, 700, 128, False, torch.bfloat16),
     (2, 2, 257, 300, 64, True, torch.float32),
     (1, 2, 1, 65, 128, False, torch.float32),
+    (1, 10, 4000, 4000, 128, True, torch.bfloat16),   # causal, 160 tiles in one 8-wave launch
 ]
 
 
