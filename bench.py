@@ -300,7 +300,10 @@ def _stats(ts) -> dict:
 class ClockSampler:
     """Reads the GPU engine (GFX) clock through amdsmi on a host thread while
     the timed steps run, so the line states the clock the kernels ran at (the
-    card lowers it under its power limit)."""
+    card lowers it under its power limit).  The firmware refreshes its metrics
+    table a few times a second, so a reading is kept only when the table's
+    firmware timestamp is new since the timed steps began: a table left over
+    from before them (idle, or the warm-up) is not counted."""
 
     def __init__(self, period_s: float = 0.02):
         self.period = period_s
@@ -317,7 +320,7 @@ class ClockSampler:
             def read():
                 m = amdsmi.amdsmi_get_gpu_metrics_info(h)
                 clks = [c for c in m["current_gfxclks"] if isinstance(c, (int, float))]
-                return (sum(clks) / len(clks), float(m["current_socket_power"]))
+                return (m.get("firmware_timestamp"), sum(clks) / len(clks), float(m["current_socket_power"]))
 
             self._read = read
             self._read()
@@ -330,14 +333,22 @@ class ClockSampler:
             return
         import threading
         self._stop = threading.Event()
+        try:
+            seen = {self._read()[0]}
+        except Exception as e:  # noqa: BLE001
+            self.error = repr(e)
+            return
 
         def run():
             while not self._stop.is_set():
                 try:
-                    self.samples.append(self._read())
+                    ts, clk, pw = self._read()
                 except Exception as e:  # noqa: BLE001
                     self.error = repr(e)
                     return
+                if ts not in seen:
+                    seen.add(ts)
+                    self.samples.append((clk, pw))
                 self._stop.wait(self.period)
 
         self._thread = threading.Thread(target=run, daemon=True)
@@ -348,14 +359,14 @@ class ClockSampler:
             self._stop.set()
             self._thread.join()
         if not self.samples:
-            return {"source": "amdsmi GFX clock", "error": self.error or "no samples"}
+            return {"source": "amdsmi GFX clock", "error": self.error or "no metrics update during the timed steps"}
         clk = _stats([c for c, _ in self.samples])
         pw = _stats([p for _, p in self.samples])
-        return {"source": "amdsmi GPU metrics (engine clock averaged over the XCDs, socket power), sampled "
-                          "every 20 ms during the timed steps",
+        return {"source": "amdsmi GPU metrics (engine clock averaged over the XCDs, socket power): the metrics-table "
+                          "updates that fell inside the timed steps",
                 "median_mhz": round(clk["median"]), "min_mhz": round(clk["min"]),
                 "max_mhz": round(max(c for c, _ in self.samples)), "median_socket_w": round(pw["median"]),
-                "samples": len(self.samples)}
+                "updates": len(self.samples)}
 
 
 def _time_calls(fn, warmup: int, reps: int, n_marks: int):
