@@ -126,8 +126,12 @@ int qk_norm_rope_out(const void *q_in, const void *k_in, void *q_out, void *k_ou
  *   k, v       bf16 [B,H,Skv,D].  Here (no workspace) v must satisfy
  *              |v| <= 65504: its fp16 conversion is exact for |v| in
  *              [2^-14, 65504], smaller magnitudes keep an absolute accuracy
- *              of 2^-25, larger ones overflow.  The workspace entry points
- *              (attn_fwd_ws and the calls built on it) take any bf16 v.
+ *              of 2^-25, larger ones overflow: a value of column d beyond
+ *              65504 turns column d of the output rows into +-inf or NaN
+ *              (the call only enqueues work, so its status cannot report
+ *              it; the other columns and the LSE are unaffected).  The
+ *              workspace entry points (attn_fwd_ws and the calls built on
+ *              it) take any bf16 v.
  *   out        [B,H,Sq,D], bf16 (out_dtype = DIT_BF16) or fp32 (DIT_FP32);
  *              must not overlap q, k, v or lse
  *   lse        fp32 [B,H,Sq], or NULL to skip it

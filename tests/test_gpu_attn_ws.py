@@ -121,6 +121,37 @@ def test_value_range_of_v_workspace_path(lo, hi):
         assert float(rel.max()) <= 2.0 ** -9
 
 
+def test_v_beyond_fp16_without_workspace_is_not_finite():
+    """Without a workspace a value of V beyond fp16's range (here 2^17 in one
+    key of column 5) makes that column of every output row non-finite (+-inf,
+    or NaN where the key's P rounds to 0), as the header states, while the
+    other columns and the LSE stay correct; the workspace path takes the same
+    V and matches the oracle, column 5 relative to its largest |v|."""
+    B, H, Sq, Skv, D = 1, 2, 300, 200, 64
+    q = inputs.random_bits(90, (B, H, Sq, D))
+    k = inputs.random_bits(91, (B, H, Skv, D))
+    v = inputs.random_bits(92, (B, H, Skv, D))
+    v[:, :, 77, 5] = inputs.to_bf16_bits(np.array([2.0 ** 17], dtype=np.float32))[0]
+    dq, dk, dv = dev_bits(q), dev_bits(k), dev_bits(v)
+    say("[attn] v beyond fp16 without a workspace")
+    o0, l0 = attn_fwd(dq, dk, dv, out_dtype=torch.float32)
+    o1, l1 = attn_fwd_ws(dq, dk, dv, _ws(B, H, Skv, D), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attn(q, k, v, 1 / math.sqrt(D), False)
+    got = host_f64(o0)
+    assert not np.isfinite(got[..., 5]).any()
+    others = [d for d in range(D) if d != 5]
+    rep = compare.attn_report(got[..., others], ref_o[..., others], host_f64(l0), ref_l, bf16=False)
+    compare.assert_ok(rep, "columns other than the out-of-range one")
+    # Workspace path: column 5 is scaled into fp16 range, so its error is
+    # relative to that column's largest |v| (as in the range tests above).
+    got1 = host_f64(o1)
+    assert np.all(np.isfinite(got1))
+    assert float(np.max(np.abs(got1[..., 5] - ref_o[..., 5]))) <= 2.0 ** -10 * 2.0 ** 17
+    rep = compare.attn_report(got1[..., others], ref_o[..., others], host_f64(l1), ref_l, bf16=False)
+    compare.assert_ok(rep, "workspace path, other columns")
+
+
 def test_value_range_of_v():
     """V spanning 2^-20 .. 2^15.9 in magnitude (P V runs on fp16 operands):
     within [2^-14, 65504] the bf16 -> fp16 conversion is exact, below it the
